@@ -1,0 +1,121 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument validation and
+// dispatch to the kernel launchers.  No allocation, no global state.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by every entry point.  Sets *empty when there is no work.
+int check_shape(int B, int H, int N, int d, float scale, bool* empty) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (*empty) return FA_OK;
+  // Element counts must fit comfortably in 64 bits and the grid in 31 bits.
+  const long long heads = (long long)B * H;
+  if (heads > (1LL << 31) / 1 || (long long)N > (1LL << 30)) return FA_ERR_INVALID_ARG;
+  if (heads * ((N + 63) / 64) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+int forward_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, const uint8_t* mask,
+                   int mask_block, bool f32, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, mask, mask_block};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // do not report an earlier, unrelated error
+  return hip_status(f32 ? fa::launch_fwd_f32(a, s) : fa::launch_fwd_bf16(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, void* stream) {
+  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, 0, false, stream);
+}
+
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, void* stream) {
+  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, 0, true, stream);
+}
+
+int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const uint8_t* block_mask, int mask_block, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, scale, &empty);
+  if (st != FA_OK) return st;
+  if (mask_block != 128) return FA_ERR_UNSUPPORTED;
+  if (empty) return FA_OK;
+  if (block_mask == nullptr) return FA_ERR_INVALID_ARG;
+  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_block, false,
+                        stream);
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, 1.0f, &empty) != FA_OK || empty) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dout) ||
+      !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned(workspace, 4) ||
+      workspace_bytes < fa_backward_workspace_size(B, H, N, d))
+    return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{q,  k,  v,  o,  dout, lse,   dq,        dk, dv, static_cast<float*>(workspace),
+                B,  H,  N,  d,  scale, causal ? 1 : 0};
+  (void)hipGetLastError();
+  return hip_status(fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* fa_error_string(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; mask block 128)";
+    case FA_ERR_HIP: return "HIP runtime error at kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+int fa_runtime_version(void) {
+  int v = -1;
+  if (hipRuntimeGetVersion(&v) != hipSuccess) return -1;
+  return v;
+}
+
+}  // extern "C"

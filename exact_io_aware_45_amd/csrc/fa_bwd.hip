@@ -1,0 +1,430 @@
+// fa_bwd.hip -- exact attention backward, bf16 in / fp32 accumulate, gfx950.
+//
+// The probabilities are recomputed tile by tile from Q, K and the saved
+// log-sum-exp instead of being stored ("FlashAttention." plate, "Never write
+// the scores": the scores are recomputed in the backward pass).  The gradient
+// formulas are the chain rule through P = softmax(S), S = scale Q K^T:
+//   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i (= sum_j P_ij dP_ij),
+//   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three launches on the caller's stream, deterministic (no atomics):
+//   1. bwd_delta: D_i = dO_i . O_i (fp32), into the caller's workspace;
+//   2. bwd_dkdv:  one workgroup per 128 keys; each wave keeps 32 keys' K and V
+//      in registers and loops over 64-query tiles of Q and dO staged in LDS:
+//      S = Q K^T and dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE),
+//      dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read from
+//      the row-major LDS tiles by transpose reads;
+//   3. bwd_dq:    one workgroup per 128 queries; each wave keeps 32 queries'
+//      Q and dO in registers and loops over 64-key tiles of K and V in LDS:
+//      S^T = K Q^T, dP^T = V dO^T (lane = query column), dS^T, and
+//      dQ^T += K^T dS^T with K^T read by transpose reads.
+#include "fa_common.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- D = dO.O
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a, long long rows) {
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int RPB = kThreads / CH;    // rows per block
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CH;
+  const int ch = threadIdx.x % CH;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(
+        reinterpret_cast<const bf16*>(a.o) + (size_t)row * D + 8 * ch);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(
+        reinterpret_cast<const bf16*>(a.dout) + (size_t)row * D + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
+  if (row < rows && ch == 0) a.delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D>
+struct DkdvTile {
+  static constexpr int BK = 128;    // keys per workgroup (4 waves x 32)
+  static constexpr int BQ = 64;     // queries per loop step
+  static constexpr int QP = D + 8;  // LDS row pitch (elements)
+  static constexpr int CH = D / 8;
+  static constexpr int LOADS = BQ * CH / kThreads;
+  static constexpr int T_ELEMS = BQ * QP;  // one tile (Q or dO)
+  static_assert(BQ * CH % kThreads == 0, "tile must split evenly");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  using T = DkdvTile<D>;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int QB = T::BQ / 32;
+
+  __shared__ __attribute__((aligned(16))) bf16 tiles[2][2][T::T_ELEMS];  // [stage][Q|dO]
+  __shared__ __attribute__((aligned(16))) float lse_s[2][T::BQ];
+  __shared__ __attribute__((aligned(16))) float del_s[2][T::BQ];
+
+  const int N = a.N;
+  const int nkt = (N + T::BK - 1) / T::BK;
+  const int total = nkt * a.B * a.H;
+  const int w = xcd_remap(blockIdx.x, total);
+  const int bh = w / nkt;
+  const int kt = w % nkt;  // small key tiles see the most queries: first
+  const int kt0 = kt * T::BK;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const size_t head = (size_t)bh * N * D;
+  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + head;
+  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
+  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
+  const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + head;
+  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
+  const float* __restrict__ DEL = a.delta + (size_t)bh * N;
+
+  // This wave's keys as B operands: K^T for S = Q K^T, V^T for dP = dO V^T.
+  const int key = kt0 + 32 * wave + l32;
+  const int kld = key < N ? key : N - 1;
+  bf16x8 kf[DC], vf[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    kf[c] = *reinterpret_cast<const bf16x8*>(K + (size_t)kld * D + 16 * c + 8 * h);
+    vf[c] = *reinterpret_cast<const bf16x8*>(V + (size_t)kld * D + 16 * c + 8 * h);
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[b][r] = 0.f;
+      dv[b][r] = 0.f;
+    }
+
+  const int nqt = (N + T::BQ - 1) / T::BQ;
+  const int qt_begin = CAUSAL ? kt0 / T::BQ : 0;
+  const float sl2 = a.scale * kLog2e;
+
+  u32x4 qreg[T::LOADS], oreg[T::LOADS];
+  float lreg = 0.f;
+  auto load_tile = [&](int qt) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int row = idx / T::CH, ch = idx % T::CH;
+      const int q = min(qt * T::BQ + row, N - 1);
+      qreg[i] = *reinterpret_cast<const u32x4*>(Q + (size_t)q * D + 8 * ch);
+      oreg[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)q * D + 8 * ch);
+    }
+    if (threadIdx.x < 2 * T::BQ) {
+      const int q = min(qt * T::BQ + (threadIdx.x % T::BQ), N - 1);
+      lreg = threadIdx.x < T::BQ ? LSE[q] * kLog2e : DEL[q];
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int row = idx / T::CH, ch = idx % T::CH;
+      lds_write16(&tiles[stage][0][row * T::QP + 8 * ch], qreg[i]);
+      lds_write16(&tiles[stage][1][row * T::QP + 8 * ch], oreg[i]);
+    }
+    if (threadIdx.x < T::BQ)
+      lse_s[stage][threadIdx.x] = lreg;
+    else if (threadIdx.x < 2 * T::BQ)
+      del_s[stage][threadIdx.x - T::BQ] = lreg;
+  };
+
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int qt = qt_begin;
+  if (qt < nqt) {
+    load_tile(qt);
+    store_tile(0);
+  }
+  __syncthreads();
+  int stage = 0;
+  for (; qt < nqt; ++qt) {
+    if (qt + 1 < nqt) load_tile(qt + 1);
+    const bf16* Qs = tiles[stage][0];
+    const bf16* Os = tiles[stage][1];
+    const int q0 = qt * T::BQ;
+    const bool need_mask = (CAUSAL && q0 < kt0 + 32 * wave + 31) || (q0 + T::BQ > N);
+
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 qa = lds_read8(Qs + (32 * qb + l32) * T::QP + 16 * c + 8 * h);
+        const bf16x8 oa = lds_read8(Os + (32 * qb + l32) * T::QP + 16 * c + 8 * h);
+        s = mfma32(qa, kf[c], s);
+        dp = mfma32(oa, vf[c], dp);
+      }
+      // s[r], dp[r]: query 32qb + 8(r/4) + 4h + r%4 of this tile, key `key`.
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * qb + 8 * g + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[stage][ql]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[stage][ql]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
+          if (need_mask) {
+            const int q = q0 + ql + e;
+            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[e]);
+        }
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over this block's queries)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 pb = pack8(s[8 * cc + 0], s[8 * cc + 1], s[8 * cc + 2], s[8 * cc + 3],
+                                s[8 * cc + 4], s[8 * cc + 5], s[8 * cc + 6], s[8 * cc + 7]);
+        const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
+                                dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
+        const int rbase = (32 * qb + 16 * cc + tr_row) * T::QP + tr_col;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const bf16x8 oa = cat8(lds_read_tr4(Os + rbase + 32 * b),
+                                 lds_read_tr4(Os + rbase + 8 * T::QP + 32 * b));
+          dv[b] = mfma32(oa, pb, dv[b]);
+          const bf16x8 qa = cat8(lds_read_tr4(Qs + rbase + 32 * b),
+                                 lds_read_tr4(Qs + rbase + 8 * T::QP + 32 * b));
+          dk[b] = mfma32(qa, db, dk[b]);
+        }
+      }
+    }
+    if (qt + 1 < nqt) store_tile(stage ^ 1);
+    __syncthreads();
+    stage ^= 1;
+  }
+
+  // dK^T, dV^T: lane holds key `key`, d = 32b + 8(r/4) + 4h + r%4.
+  if (key < N) {
+    bf16* dkrow = reinterpret_cast<bf16*>(a.dk) + head + (size_t)key * D;
+    bf16* dvrow = reinterpret_cast<bf16*>(a.dv) + head + (size_t)key * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = to_bf16(dk[b][4 * g + e] * a.scale);
+          v4[e] = to_bf16(dv[b][4 * g + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dkrow + 32 * b + 8 * g + 4 * h) = k4;
+        *reinterpret_cast<bf16x4*>(dvrow + 32 * b + 8 * g + 4 * h) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------- dQ
+template <int D>
+struct DqTile {
+  static constexpr int BQ = 128;    // queries per workgroup (4 waves x 32)
+  static constexpr int BK = 64;     // keys per loop step
+  static constexpr int KP = D + 8;  // LDS row pitch (elements)
+  static constexpr int CH = D / 8;
+  static constexpr int LOADS = BK * CH / kThreads;
+  static constexpr int T_ELEMS = BK * KP;
+  static_assert(BK * CH % kThreads == 0, "tile must split evenly");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdArgs a) {
+  using T = DqTile<D>;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NB = T::BK / 32;
+
+  __shared__ __attribute__((aligned(16))) bf16 tiles[2][2][T::T_ELEMS];  // [stage][K|V]
+
+  const int N = a.N;
+  const int nqt = (N + T::BQ - 1) / T::BQ;
+  const int total = nqt * a.B * a.H;
+  const int w = xcd_remap(blockIdx.x, total);
+  const int bh = w / nqt;
+  const int qt = CAUSAL ? (nqt - 1 - w % nqt) : (w % nqt);
+  const int q0 = qt * T::BQ;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const size_t head = (size_t)bh * N * D;
+  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + head;
+  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
+  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
+  const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + head;
+
+  const int qrow = q0 + 32 * wave + l32;
+  const int qld = qrow < N ? qrow : N - 1;
+  bf16x8 qf[DC], of[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    qf[c] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qld * D + 16 * c + 8 * h);
+    of[c] = *reinterpret_cast<const bf16x8*>(dO + (size_t)qld * D + 16 * c + 8 * h);
+  }
+  const float lse2 = a.lse[(size_t)bh * N + qld] * kLog2e;
+  const float dlt = a.delta[(size_t)bh * N + qld];
+  const float sl2 = a.scale * kLog2e;
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[b][r] = 0.f;
+
+  const int nt = (N + T::BK - 1) / T::BK;
+  const int qmax = min(q0 + T::BQ, N) - 1;
+  const int tend = CAUSAL ? min(nt, qmax / T::BK + 1) : nt;
+
+  u32x4 kreg[T::LOADS], vreg[T::LOADS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int row = idx / T::CH, ch = idx % T::CH;
+      const int k = min(t * T::BK + row, N - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(K + (size_t)k * D + 8 * ch);
+      vreg[i] = *reinterpret_cast<const u32x4*>(V + (size_t)k * D + 8 * ch);
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int row = idx / T::CH, ch = idx % T::CH;
+      lds_write16(&tiles[stage][0][row * T::KP + 8 * ch], kreg[i]);
+      lds_write16(&tiles[stage][1][row * T::KP + 8 * ch], vreg[i]);
+    }
+  };
+
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int t = 0;
+  if (t < tend) {
+    load_tile(t);
+    store_tile(0);
+  }
+  __syncthreads();
+  int stage = 0;
+  for (; t < tend; ++t) {
+    if (t + 1 < tend) load_tile(t + 1);
+    const bf16* Ks = tiles[stage][0];
+    const bf16* Vs = tiles[stage][1];
+    const int k0 = t * T::BK;
+    const bool need_mask = (CAUSAL && k0 + T::BK - 1 > q0 + 32 * wave) || (k0 + T::BK > N);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 ka = lds_read8(Ks + (32 * kb + l32) * T::KP + 16 * c + 8 * h);
+        const bf16x8 va = lds_read8(Vs + (32 * kb + l32) * T::KP + 16 * c + 8 * h);
+        s = mfma32(ka, qf[c], s);
+        dp = mfma32(va, of[c], dp);
+      }
+      // s[r], dp[r]: key k0 + 32kb + 8(r/4) + 4h + r%4, query qrow.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], sl2, -lse2));
+        if (need_mask) {
+          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+        }
+        dp[r] = p * (dp[r] - dlt);
+      }
+      // dQ^T += K^T dS^T (contraction over this block's keys)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
+                                dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
+        const int rbase = (32 * kb + 16 * cc + tr_row) * T::KP + tr_col;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const bf16x8 ka = cat8(lds_read_tr4(Ks + rbase + 32 * b),
+                                 lds_read_tr4(Ks + rbase + 8 * T::KP + 32 * b));
+          dq[b] = mfma32(ka, db, dq[b]);
+        }
+      }
+    }
+    if (t + 1 < tend) store_tile(stage ^ 1);
+    __syncthreads();
+    stage ^= 1;
+  }
+
+  if (qrow < N) {
+    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + head + (size_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = to_bf16(dq[b][4 * g + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dqrow + 32 * b + 8 * g + 4 * h) = v4;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  constexpr int RPB = kThreads / (D / 8);
+  const long long g0 = (rows + RPB - 1) / RPB;
+  const long long g1 = (long long)((a.N + DkdvTile<D>::BK - 1) / DkdvTile<D>::BK) * a.B * a.H;
+  const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
+  if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)g0), dim3(kThreads), 0, s, a, rows);
+  if (a.causal) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 128) return launch_d<128>(a, s);
+  if (a.d == 64) return launch_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

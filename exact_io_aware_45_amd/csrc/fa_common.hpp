@@ -1,0 +1,102 @@
+// fa_common.hpp -- device-side building blocks shared by the attention kernels
+// (gfx950 / CDNA4 only).
+//
+// Register layouts of the two bf16 matrix instructions used here (measured on
+// the device, lane l of a 64-wide wave, h = l / 32):
+//   v_mfma_f32_32x32x16_bf16:  A[i][k]: i = l % 32, k = 8h + t   (t = 0..7)
+//                              B[k][j]: j = l % 32, k = 8h + t
+//                              C[i][j]: j = l % 32, i = 8(r/4) + 4h + r%4
+//                              (r = 0..15 accumulator registers)
+//   v_mfma_f32_16x16x32_bf16:  A[i][k]: i = l % 16, k = 8(l/16) + t
+//                              B[k][j]: j = l % 16, k = 8(l/16) + t
+//                              C[i][j]: j = l % 16, i = 4(l/16) + r
+// ds_read_b64_tr_b16 (LDS transpose read): within each group of 16 lanes, lane
+// i receives element (i % 4) of the 4-element chunk addressed by lane
+// 4t + i/4, for t = 0..3.  If lane j = 4t + s of a group points at row
+// (r0 + t), columns (c0 + 4s .. c0 + 4s + 3) of a row-major tile, lane i gets
+// rows r0..r0+3 of column c0 + i: a column segment of the tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS load (one MFMA operand of 8 bf16).
+__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
+  return *(const FA_LDS bf16x8*)(p);
+}
+
+__device__ __forceinline__ void lds_write16(bf16* p, u32x4 v) {
+  *(FA_LDS u32x4*)(p) = v;
+}
+
+// Transposed 8-byte LDS read (see the layout note at the top of the file).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Reductions across the two halves of the wave (lanes l and l ^ 32) with one
+// v_permlane32_swap: given x in both operands, lanes 0..31 receive
+// (x[l], x[l+32]) and lanes 32..63 receive (x[l-32], x[l]).
+__device__ __forceinline__ float half_pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+__device__ __forceinline__ float half_pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// f32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                        float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+  return r;
+}
+
+// Workgroup index -> work item, so that consecutive items stay on one XCD
+// (the hardware deals workgroups to the 8 XCDs round-robin; each XCD has its
+// own L2, and items of one head reuse the same K/V).  Falls back to identity
+// when the count does not split evenly.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int kXcd = 8;
+  if (total % kXcd != 0) return wg;
+  const int per = total / kXcd;
+  return (wg % kXcd) * per + wg / kXcd;
+}
+
+}  // namespace fa

@@ -1,0 +1,44 @@
+// fa_internal.hpp -- host-side launch interface between the C ABI (fa_api.hip)
+// and the kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Problem description shared by every forward launch.  Tensors are contiguous
+// [B][H][N][d]; lse is [B][H][N] fp32.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  const uint8_t* mask;  // tile mask [nmb][nmb] or nullptr
+  int mask_block;       // tile edge of the mask (keys and queries)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: D_i = dO_i . O_i, [B][H][N] fp32
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

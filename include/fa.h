@@ -1,0 +1,127 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * The operation is exact attention, O = softmax(scale * Q K^T) V, computed
+ * tile by tile on chip with an online softmax so that the N x N score matrix
+ * never reaches HBM ("FlashAttention." plate, opening section and "Never
+ * write the scores"; "FlashAttention: Fast and Memory-Efficient Exact
+ * Attention with IO-Awareness", Abstract).  The result is the standard
+ * attention result up to floating-point rounding (same plate, "Never write
+ * the scores").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout     Q, K, V, O, dO, dQ, dK, dV are dense, contiguous [B][H][N][d]
+ *             tensors (row-major, d fastest).  LSE is [B][H][N] fp32, the
+ *             natural-log log-sum-exp of row i of the scaled, masked scores.
+ *  Memory     every tensor pointer is a DEVICE pointer on the current HIP
+ *             device; `block_mask` is a device pointer too.  The caller owns
+ *             every buffer (inputs, outputs, workspace); the library never
+ *             allocates or frees memory and keeps no global state, so it is
+ *             re-entrant.  Buffers must not overlap.
+ *  Streams    `stream` is a hipStream_t passed as void* (NULL = the null
+ *             stream).  Calls are asynchronous: they enqueue kernels on the
+ *             stream and return; buffers must stay alive until it syncs.
+ *  Alignment  tensor pointers must be 16-byte aligned; LSE and the workspace
+ *             4-byte aligned.
+ *  Sizes      B, H, N >= 0; d in {64, 128}.  If B*H*N == 0 the call does
+ *             nothing and returns FA_OK (pointers may then be NULL).
+ *  scale      finite and > 0 (1/sqrt(d) is the usual choice).
+ *  causal     nonzero: key j is visible to query i only if j <= i.
+ *  Masks      a fully masked row yields O = 0 and LSE = -infinity.
+ *  Errors     status codes only; nothing is thrown across the ABI.  Argument
+ *             errors are detected before anything is enqueued.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad scale, misalignment */
+  FA_ERR_UNSUPPORTED = 2, /* valid request outside what is built (d, mask block) */
+  FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Forward pass, bf16 storage, fp32 accumulation.
+ *   q, k, v  in : bf16 [B][H][N][d]
+ *   o        out: bf16 [B][H][N][d]
+ *   lse      out: fp32 [B][H][N]   (saved for fa_backward)
+ * The scores are tiled through LDS and registers and never written to HBM
+ * ("FlashAttention." plate, opening section).
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Forward pass with fp32 inputs, arithmetic and outputs (q, k, v, o fp32),
+ * for small problems that need fp32 accuracy.  Same arguments as fa_forward.
+ */
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace fa_backward needs for this shape (the per-row
+ * D_i = dO_i . O_i, fp32 [B][H][N]).  Returns 0 for empty or invalid shapes.
+ */
+size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass, bf16 storage, fp32 accumulation.  The probabilities are
+ * recomputed tile by tile from Q, K and the saved LSE instead of being stored
+ * ("FlashAttention." plate, "Never write the scores": the backward recomputes
+ * the scores).  Gradients by the chain rule through P = softmax(S):
+ *   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, o, dout in : bf16 [B][H][N][d]  (o and lse from fa_forward with
+ *                         the same q, k, v, scale and causal flag)
+ *   lse              in : fp32 [B][H][N]
+ *   dq, dk, dv       out: bf16 [B][H][N][d]
+ *   workspace        scratch device memory of at least
+ *                    fa_backward_workspace_size(B, H, N, d) bytes, owned by
+ *                    the caller; its contents on entry do not matter.
+ * Deterministic: no atomics; the same inputs give bitwise the same outputs.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                void* stream);
+
+/*
+ * Block-sparse forward: like fa_forward, but scores in tiles whose mask entry
+ * is 0 are -infinity, and such tiles are skipped entirely (no loads, no
+ * matrix work): "Flash Attention: IO-Aware Attention Computation", paragraph
+ * on block-sparse attention; "FlashAttention: Fast and Memory-Efficient Exact
+ * Attention with IO-Awareness", Abstract.
+ *   block_mask  in: uint8 device array [nb][nb], nb = ceil(N / mask_block);
+ *               entry [qb][kb] != 0 means query tile qb attends to key tile
+ *               kb.  One mask is shared by every batch and head.
+ *   mask_block  tile edge in tokens; must be 128 (FA_ERR_UNSUPPORTED
+ *               otherwise).
+ * causal may be combined with the mask (both apply).
+ */
+int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const uint8_t* block_mask, int mask_block, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fa_error_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/* hipRuntimeGetVersion() of the HIP runtime the library is running on, or -1. */
+int fa_runtime_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle,
+element by element, on seeded synthetic inputs.
+
+Small cases span several tiles and a ragged tail and are compared in full.
+The five full-size workloads run in the same launch configuration the
+benchmark times; their outputs are compared on sampled (batch, head) pairs,
+which the oracle computes completely (heads are independent).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_45_amd import _lib, inputs
+from _parity import check, check_lse, log, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+
+
+def run_forward(q, k, v, causal, mask=None):
+    if mask is None:
+        o, lse = _lib.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    else:
+        o, lse = _lib.forward_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV),
+                                          causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def heads_of(t, pairs):
+    """fp64 numpy [len(pairs), N, d] of the selected (b, h) pairs."""
+    return np.stack([to64(t[b, h]) for b, h in pairs])
+
+
+def all_pairs(t):
+    return [(b, h) for b in range(t.shape[0]) for h in range(t.shape[1])]
+
+
+def sample_pairs(B, H, n, seed=0):
+    rng = np.random.default_rng(seed)
+    flat = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [(int(i) // H, int(i) % H) for i in sorted(flat)]
+
+
+def forward_parity(q, k, v, causal, pairs, mask=None, bf16=True):
+    o, lse = run_forward(q, k, v, causal, mask)
+    scale = q.shape[-1] ** -0.5
+    ro, rl = oracle.forward(heads_of(q, pairs), heads_of(k, pairs), heads_of(v, pairs), scale,
+                            causal, block_mask=None if mask is None else mask.numpy(),
+                            mask_block=128)
+    go = np.stack([to64(o[b, h]) for b, h in pairs])
+    gl = torch.stack([lse[b, h] for b, h in pairs])
+    check("O", go, ro, bf16)
+    check_lse(gl, rl, bf16)
+    return o, lse
+
+
+# ------------------------------------------------------------------ forward
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 63, 65, 129, 200, 333])
+def test_forward_bf16_small(N, d, causal):
+    need_gpu()
+    log(f"forward bf16 B2 H3 N{N} d{d} causal={causal}")
+    q, k, v = inputs.qkv(2, 3, N, d, torch.bfloat16, seed=N + d)
+    forward_parity(q, k, v, causal, all_pairs(q))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 128, 150])
+def test_forward_f32_small(N, d, causal):
+    need_gpu()
+    log(f"forward f32 B2 H2 N{N} d{d} causal={causal}")
+    q, k, v = inputs.qkv(2, 2, N, d, torch.float32, seed=7 * N + d)
+    forward_parity(q, k, v, causal, all_pairs(q), bf16=False)
+
+
+def test_forward_f32_single_head_workload():
+    need_gpu()
+    w = inputs.WORKLOADS["single_head_f32"]
+    for seed in (0, 1, 2):
+        log(f"{w.name} seed {seed}")
+        x = inputs.workload_inputs(w, seed)
+        forward_parity(x["q"], x["k"], x["v"], w.causal, all_pairs(x["q"]), bf16=False)
+
+
+@pytest.mark.parametrize("name", ["batched_d64", "batched_d64_causal", "long_d128_causal"])
+def test_forward_full_workloads(name):
+    need_gpu()
+    w = inputs.WORKLOADS[name]
+    for seed in (0, 1):
+        log(f"{name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal})")
+        x = inputs.workload_inputs(w, seed)
+        forward_parity(x["q"], x["k"], x["v"], w.causal, sample_pairs(w.B, w.H, 4, seed))
+
+
+def test_causal_row_zero_is_v0_exactly():
+    need_gpu()
+    q, k, v = inputs.qkv(2, 2, 300, 128, torch.bfloat16, seed=3)
+    o, lse = run_forward(q, k, v, True)
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_forward_on_a_side_stream_matches_default_stream():
+    need_gpu()
+    q, k, v = (t.to(DEV) for t in inputs.qkv(2, 4, 777, 128, torch.bfloat16, seed=5))
+    o1, l1 = _lib.forward(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2, l2 = _lib.forward(q, k, v, causal=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forward_allocates_nothing_quadratic():
+    need_gpu()
+    B, H, N, d = 1, 8, 8192, 128
+    q, k, v = (t.to(DEV) for t in inputs.qkv(B, H, N, d, torch.bfloat16, seed=0))
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    o, lse = _lib.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    outputs = o.numel() * 2 + lse.numel() * 4
+    log(f"  peak extra {extra} B, outputs {outputs} B, one score matrix {N * N * 2} B")
+    assert extra <= outputs + (1 << 20)
+
+
+# ----------------------------------------------------------------- backward
+def backward_parity(q, k, v, do, causal, pairs):
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = _lib.forward(qd, kd, vd, causal=causal)
+    dq, dk, dv = _lib.backward(qd, kd, vd, o, dod, lse, causal=causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    scale = q.shape[-1] ** -0.5
+    rdq, rdk, rdv, _, _ = oracle.backward(heads_of(q, pairs), heads_of(k, pairs),
+                                          heads_of(v, pairs), heads_of(do, pairs), scale, causal)
+    for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        check(name, np.stack([to64(g[b, h]) for b, h in pairs]), r)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 40, 64, 129, 200, 333])
+def test_backward_small(N, d, causal):
+    need_gpu()
+    log(f"backward B2 H2 N{N} d{d} causal={causal}")
+    q, k, v, do = inputs.qkv(2, 2, N, d, torch.bfloat16, seed=11 * N + d, with_dout=True)
+    backward_parity(q, k, v, do, causal, all_pairs(q))
+
+
+def test_backward_full_workload():
+    need_gpu()
+    w = inputs.WORKLOADS["bwd_d128_causal"]
+    for seed in (0, 1):
+        log(f"{w.name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal})")
+        x = inputs.workload_inputs(w, seed)
+        backward_parity(x["q"], x["k"], x["v"], x["dout"], w.causal,
+                        sample_pairs(w.B, w.H, 4, seed))
+
+
+def test_backward_is_deterministic():
+    need_gpu()
+    q, k, v, do = (t.to(DEV) for t in inputs.qkv(2, 4, 1000, 128, torch.bfloat16, seed=9,
+                                                 with_dout=True))
+    outs = []
+    for _ in range(3):
+        o, lse = _lib.forward(q, k, v, causal=True)
+        outs.append((o, lse) + _lib.backward(q, k, v, o, do, lse, causal=True))
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- block-sparse
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 300, 700])
+def test_blocksparse_small(N, d, causal):
+    need_gpu()
+    log(f"block-sparse B2 H2 N{N} d{d} causal={causal}")
+    q, k, v = inputs.qkv(2, 2, N, d, torch.bfloat16, seed=13 * N + d)
+    nb = -(-N // 128)
+    g = torch.Generator().manual_seed(N)
+    mask = (torch.rand(nb, nb, generator=g) < 0.5).to(torch.uint8)
+    if nb > 1:
+        mask[1, :] = 0  # an empty mask row: O = 0, LSE = -inf
+    forward_parity(q, k, v, causal, all_pairs(q), mask=mask)
+
+
+def test_blocksparse_full_workload():
+    need_gpu()
+    w = inputs.WORKLOADS["blocksparse_d64"]
+    for seed in (0, 1):
+        x = inputs.workload_inputs(w, seed)
+        log(f"{w.name} seed {seed}: {int(x['mask'].sum())} of {x['mask'].numel()} tiles")
+        forward_parity(x["q"], x["k"], x["v"], w.causal, sample_pairs(w.B, w.H, 4, seed),
+                       mask=x["mask"])
+
+
+def test_blocksparse_mask_identities():
+    need_gpu()
+    N = 1000
+    nb = -(-N // 128)
+    q, k, v = inputs.qkv(1, 4, N, 64, torch.bfloat16, seed=21)
+    od, ld = run_forward(q, k, v, False)
+    o1, l1 = run_forward(q, k, v, False, mask=torch.ones(nb, nb, dtype=torch.uint8))
+    assert torch.equal(od, o1) and torch.equal(ld, l1)
+    oc, lc = run_forward(q, k, v, True)
+    tri = torch.ones(nb, nb, dtype=torch.uint8).tril()
+    o2, l2 = run_forward(q, k, v, True, mask=tri)
+    assert torch.equal(oc, o2) and torch.equal(lc, l2)
+    o3, l3 = run_forward(q, k, v, False, mask=torch.zeros(nb, nb, dtype=torch.uint8))
+    assert torch.all(o3 == 0) and torch.all(torch.isneginf(l3))
