@@ -59,20 +59,19 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Reductions across the two halves of the wave (lanes l and l ^ 32) with one
-// v_permlane32_swap: given x in both operands, lanes 0..31 receive
-// (x[l], x[l+32]) and lanes 32..63 receive (x[l-32], x[l]).
-__device__ __forceinline__ float half_pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+// Reductions across the two halves of the wave (lanes l and l ^ 32), through
+// ds_bpermute_b32.  (v_permlane32_swap would do this in one VALU op, but the
+// ROCm 7.2 compiler miscompiles its second result when the two results are
+// consumed separately -- it reuses the first result's register -- so it is
+// not used.)
+__device__ __forceinline__ float other_half(float x) {
+  const int src = ((int)(threadIdx.x & 63) ^ 32) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
 }
 
-__device__ __forceinline__ float half_pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                            __builtin_bit_cast(uint32_t, x), false, false);
-  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
-}
+__device__ __forceinline__ float half_pair_max(float x) { return fmaxf(x, other_half(x)); }
+
+__device__ __forceinline__ float half_pair_sum(float x) { return x + other_half(x); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
