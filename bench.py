@@ -1,0 +1,194 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = fa_forward + fa_backward (the whole forward/backward path) on the
+long causal workload: B=1, H=32, N=8192, d=128, bf16, causal, inputs already
+resident in HBM.  Timing uses HIP events on the stream the kernels run on.
+Prints ONE JSON line:
+  value        whole-step TFLOP/s with the algorithmic FLOP counts
+               forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, both halved for causal
+  fwd / bwd    each pass's own time, TFLOP/s and fraction of the bf16 MFMA peak
+  roofline     the forward kernel (one launch per fa_forward) against the bf16
+               dense MFMA peak; the backward call gets the same treatment in
+               roofline_bwd
+  cpu_baseline the fp64 CPU oracle, timed on this host on a bounded sample of
+               the same workload (whole heads, forward + backward)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense; published 2.5 PF)
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(w, which: str) -> float:
+    base = w.B * w.H * float(w.N) ** 2 * w.d
+    f = {"fwd": 4.0, "bwd": 10.0}[which] * base
+    return f / 2 if w.causal else f
+
+
+def traffic_bytes(w, which: str) -> float:
+    """Algorithmic HBM bytes of one call: read the inputs once, write the outputs once."""
+    t = w.B * w.H * w.N * w.d * 2.0  # one bf16 tensor
+    rows = w.B * w.H * w.N * 4.0     # one fp32 [B,H,N] vector
+    if which == "fwd":
+        return 3 * t + t + rows                 # Q K V in, O + LSE out
+    return 5 * t + rows + 3 * t + 2 * rows      # Q K V O dO + LSE in; dQ dK dV out; D out/in
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0, max_heads: int = 8):
+    """Time the fp64 oracle (forward + backward of whole heads) on the host cores."""
+    import oracle
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    done, t_total = 0, 0.0
+    while done < max_heads and t_total < budget_s:
+        b, h = divmod(done, w.H)
+        t0 = time.perf_counter()
+        oracle.forward(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
+        oracle.backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+    per_head = (flops(w, "fwd") + flops(w, "bwd")) / (w.B * w.H)
+    return {"value": round(per_head * done / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{done} whole head(s) of the workload (forward + backward, all "
+                      f"{w.N} rows), {t_total:.1f} s, fp64, same FLOP convention"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters, if present")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from exact_io_aware_45_amd import _lib, inputs
+
+    w = inputs.WORKLOADS["long_d128_causal"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _lib.load()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    host = inputs.qkv(w.B, w.H, w.N, w.d, w.torch_dtype, args.seed, with_dout=True)
+    inp = dict(zip(("q", "k", "v", "dout"), host))
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    ws = torch.empty(max(1, _lib.backward_workspace_size(w.B, w.H, w.N, w.d)), dtype=torch.uint8,
+                     device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        o, lse = _lib.forward(q, k, v, causal=w.causal)
+        if ev is not None:
+            ev[1].record()
+        _lib.backward(q, k, v, o, do, lse, causal=w.causal, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_per_step = total_ms / args.steps
+
+    ff, fb = flops(w, "fwd"), flops(w, "bwd")
+    value = (ff + fb) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
+
+    traffic = {}
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            traffic = json.load(f)
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak, N=8192 d=128 causal",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (i.i.d. N(0,1) Q, K, V, dO from a seeded generator)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "pass": "forward+backward", "seed": args.seed},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
+                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "flops": ff},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+                "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "flops": fb},
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic.get("fwd_bf16_kernel"),
+                     "kernel": "fwd_bf16_kernel<d=128, BC=64, causal> (1 launch per fa_forward)",
+                     "flops_per_launch": ff, "avg_launch_ms": round(fwd_ms, 4),
+                     "algorithmic_bytes_per_launch": traffic_bytes(w, "fwd")},
+        "roofline_bwd": {"bound": "mfma", "achieved": round(bwd_tf, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic.get("fa_backward"),
+                         "kernel": "fa_backward call = bwd_delta + bwd_dkdv + bwd_dq launches",
+                         "flops_per_call": fb, "avg_call_ms": round(bwd_ms, 4),
+                         "algorithmic_bytes_per_call": traffic_bytes(w, "bwd")},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "hip_runtime": _lib.runtime_version(), "libfa": _lib.version()},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

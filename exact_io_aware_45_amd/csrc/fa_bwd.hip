@@ -150,6 +150,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  wait_global_loads();  // K, V operands resident before the query loop
   int qt = qt_begin;
   if (qt < nqt) {
     load_tile(qt);
@@ -328,6 +329,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  wait_global_loads();  // Q, dO operands resident before the key loop
   int t = 0;
   if (t < tend) {
     load_tile(t);

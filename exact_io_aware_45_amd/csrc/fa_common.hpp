@@ -55,6 +55,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + x.x + x.y in fp32 (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float dot2_ones(bf16x2 x, float acc) {
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+}
+
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -72,6 +80,13 @@ __device__ __forceinline__ float other_half(float x) {
 __device__ __forceinline__ float half_pair_max(float x) { return fmaxf(x, other_half(x)); }
 
 __device__ __forceinline__ float half_pair_sum(float x) { return x + other_half(x); }
+
+// Wait until every global load this wave has issued has returned
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their no-wait maxima).
+// Used after loading register-resident operands before a loop, so that the
+// loop's own prefetch loads are not waited on by the first use of those
+// operands: the vector-memory counter retires in order.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

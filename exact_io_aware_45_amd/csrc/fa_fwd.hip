@@ -20,7 +20,7 @@
 //     tile's math;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //     wave's Q held in registers), so that every lane owns one query column:
-//     the row max and row sum are in-register plus one v_permlane32_swap;
+//     the row max and row sum are in-register plus one cross-half exchange;
 //   * P goes from the S^T accumulators straight into the B operand of
 //     O^T += V^T P^T; the V^T operand is read from the row-major V tile with
 //     the LDS transpose read (ds_read_b64_tr_b16), in the key order the
@@ -148,6 +148,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   float l_run = 0.f;        // running sum over this lane's keys
   const float sl2 = a.scale * kLog2e;
 
+  wait_global_loads();  // Q operands resident before the key loop
   int t = next_tile(0);
   if (t < tend) {
     load_tile(t);
