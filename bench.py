@@ -46,6 +46,32 @@ def traffic_bytes(w, which: str) -> float:
     return 5 * t + rows + 3 * t + 2 * rows      # Q K V O dO + LSE in; dQ dK dV out; D out/in
 
 
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ("fa_fwd.hip", "fa_common.hpp"),
+    "fa_backward": ("fa_bwd.hip", "fa_common.hpp"),
+}
+
+
+def source_sha(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(path: str) -> dict:
+    """Counter-measured HBM bytes per launch, kept only for unchanged kernel sources."""
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        t = json.load(f)
+    shas = t.get("source_sha", {})
+    return {k: t[k] for k, files in KERNEL_SOURCES.items()
+            if k in t and shas.get(k) == source_sha(files)}
+
+
 def cpu_baseline(w, inp, budget_s: float = 12.0, max_heads: int = 8):
     """Time the fp64 oracle (forward + backward of whole heads) on the host cores."""
     import oracle
@@ -142,10 +168,7 @@ def main():
     fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
     bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
 
-    traffic = {}
-    if os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            traffic = json.load(f)
+    traffic = load_traffic(args.traffic_json)
 
     props = torch.cuda.get_device_properties(dev)
     line = {
