@@ -142,7 +142,7 @@ def backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
              workspace=None):
-    """fa_backward: returns (dq, dk, dv), bf16."""
+    """fa_backward: returns (dq, dk, dv), fp32."""
     lib = load()
     B, H, N, d = _shape(q, k, v, torch.bfloat16)
     for name, t in (("o", o), ("dout", dout)):
@@ -154,7 +154,7 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
     ws_bytes = backward_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
     _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                            _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d,
                            _scale(scale, d), int(bool(causal)), _stream(q.device)),

@@ -21,9 +21,9 @@ int check_shape(int B, int H, int N, int d, float scale, bool* empty) {
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   *empty = (B == 0 || H == 0 || N == 0);
   if (*empty) return FA_OK;
-  // Element counts must fit comfortably in 64 bits and the grid in 31 bits.
+  // Every launch has at most one workgroup per 64 rows of each head; the
+  // grid must fit in 31 bits.  (Element offsets are computed in 64 bits.)
   const long long heads = (long long)B * H;
-  if (heads > (1LL << 31) / 1 || (long long)N > (1LL << 30)) return FA_ERR_INVALID_ARG;
   if (heads * ((N + 63) / 64) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
@@ -81,7 +81,7 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d) {
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                const float* lse, float* dq, float* dk, float* dv, void* workspace,
                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                 void* stream) {
   bool empty = false;

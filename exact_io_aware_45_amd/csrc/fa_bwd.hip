@@ -7,9 +7,13 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i (= sum_j P_ij dP_ij),
 //   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
+// Gradients are written in fp32: rounding them to bf16 alone would cost up
+// to half a bf16 ulp (2^-6 for values in [4, 8), 2^-5 above 8), which is
+// most of the 2e-2 absolute error budget the results are checked against.
+//
 // Three launches on the caller's stream, deterministic (no atomics):
 //   1. bwd_delta: D_i = dO_i . O_i (fp32), into the caller's workspace;
-//   2. bwd_dkdv:  one workgroup per 128 keys; each wave keeps 32 keys' K and V
+//   2. bwd_dkdv:  one workgroup per 256 keys; each wave keeps 32 keys' K and V
 //      in registers and loops over 64-query tiles of Q and dO staged in LDS:
 //      S = Q K^T and dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE),
 //      dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read from
@@ -50,21 +54,24 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a, long lon
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <int D>
+// NW waves per workgroup, 32 keys per wave; 64-query tiles of Q and dO are
+// staged in swizzled LDS tiles (read row-wise for S = Q K^T and dP = dO V^T,
+// and column-wise by transpose reads for dV^T += dO^T P and dK^T += Q^T dS).
+template <int D, int NW>
 struct DkdvTile {
-  static constexpr int BK = 128;    // keys per workgroup (4 waves x 32)
-  static constexpr int BQ = 64;     // queries per loop step
-  static constexpr int QP = D + 8;  // LDS row pitch (elements)
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BK = 32 * NW;  // keys per workgroup
+  static constexpr int BQ = 64;       // queries per loop step
   static constexpr int CH = D / 8;
-  static constexpr int LOADS = BQ * CH / kThreads;
-  static constexpr int T_ELEMS = BQ * QP;  // one tile (Q or dO)
-  static_assert(BQ * CH % kThreads == 0, "tile must split evenly");
+  static constexpr int LOADS = BQ * CH / THREADS;
+  static constexpr int T_ELEMS = BQ * D;  // one tile (Q or dO), unpadded
+  static_assert(BQ * CH % THREADS == 0, "tile must split evenly");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void bwd_dkdv_kernel(BwdArgs a) {
-  using T = DkdvTile<D>;
+  using T = DkdvTile<D, NW>;
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = T::BQ / 32;
@@ -122,11 +129,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto load_tile = [&](int qt) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      const int q = min(qt * T::BQ + row, N - 1);
-      qreg[i] = *reinterpret_cast<const u32x4*>(Q + (size_t)q * D + 8 * ch);
-      oreg[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)q * D + 8 * ch);
+      const int idx = threadIdx.x + T::THREADS * i;
+      const int q = min(qt * T::BQ + idx / T::CH, N - 1);
+      qreg[i] = *reinterpret_cast<const u32x4*>(Q + (size_t)q * D + 8 * (idx % T::CH));
+      oreg[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)q * D + 8 * (idx % T::CH));
     }
     if (threadIdx.x < 2 * T::BQ) {
       const int q = min(qt * T::BQ + (threadIdx.x % T::BQ), N - 1);
@@ -136,10 +142,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto store_tile = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      lds_write16(&tiles[stage][0][row * T::QP + 8 * ch], qreg[i]);
-      lds_write16(&tiles[stage][1][row * T::QP + 8 * ch], oreg[i]);
+      const int idx = threadIdx.x + T::THREADS * i;
+      const int off = tile_off<D>(idx / T::CH, idx % T::CH);
+      lds_write16(&tiles[stage][0][off], qreg[i]);
+      lds_write16(&tiles[stage][1][off], oreg[i]);
     }
     if (threadIdx.x < T::BQ)
       lse_s[stage][threadIdx.x] = lreg;
@@ -147,8 +153,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
       del_s[stage][threadIdx.x - T::BQ] = lreg;
   };
 
+  // Per-lane swizzle terms.  Row-wise operand reads: row 32qb + l32, chunk
+  // 2c + h.  Transpose reads: rows 32qb + 16cc + tr_row (+8), chunk
+  // 4b + (tr_col >> 3), element (tr_col & 7) within the chunk.
+  const int sw_row = tile_swz<D>(l32);
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
+  const int tq = tr_col >> 3, te = tr_col & 7;
+  auto tr_off = [&](int row, int sw, int b) {
+    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+  };
 
   wait_global_loads();  // K, V operands resident before the query loop
   int qt = qt_begin;
@@ -173,12 +188,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
         s[r] = 0.f;
         dp[r] = 0.f;
       }
+      const int rrow = (32 * qb + l32) * D;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const bf16x8 qa = lds_read8(Qs + (32 * qb + l32) * T::QP + 16 * c + 8 * h);
-        const bf16x8 oa = lds_read8(Os + (32 * qb + l32) * T::QP + 16 * c + 8 * h);
-        s = mfma32(qa, kf[c], s);
-        dp = mfma32(oa, vf[c], dp);
+        const int off = rrow + 8 * ((2 * c + h) ^ sw_row);
+        s = mfma32(lds_read8(Qs + off), kf[c], s);
+        dp = mfma32(lds_read8(Os + off), vf[c], dp);
       }
       // s[r], dp[r]: query 32qb + 8(r/4) + 4h + r%4 of this tile, key `key`.
 #pragma unroll
@@ -205,15 +220,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
                                 s[8 * cc + 4], s[8 * cc + 5], s[8 * cc + 6], s[8 * cc + 7]);
         const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
                                 dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
-        const int rbase = (32 * qb + 16 * cc + tr_row) * T::QP + tr_col;
+        const int r_lo = 32 * qb + 16 * cc + tr_row;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const bf16x8 oa = cat8(lds_read_tr4(Os + rbase + 32 * b),
-                                 lds_read_tr4(Os + rbase + 8 * T::QP + 32 * b));
-          dv[b] = mfma32(oa, pb, dv[b]);
-          const bf16x8 qa = cat8(lds_read_tr4(Qs + rbase + 32 * b),
-                                 lds_read_tr4(Qs + rbase + 8 * T::QP + 32 * b));
-          dk[b] = mfma32(qa, db, dk[b]);
+          const int o_lo = tr_off(r_lo, sw_lo, b), o_hi = tr_off(r_lo + 8, sw_hi, b);
+          dv[b] = mfma32(cat8(lds_read_tr4(Os + o_lo), lds_read_tr4(Os + o_hi)), pb, dv[b]);
+          dk[b] = mfma32(cat8(lds_read_tr4(Qs + o_lo), lds_read_tr4(Qs + o_hi)), db, dk[b]);
         }
       }
     }
@@ -222,40 +234,48 @@ void bwd_dkdv_kernel(BwdArgs a) {
     stage ^= 1;
   }
 
-  // dK^T, dV^T: lane holds key `key`, d = 32b + 8(r/4) + 4h + r%4.
+  // dK^T, dV^T (fp32 out): lane holds key `key`, d = 32b + 8(r/4) + 4h + r%4.
   if (key < N) {
-    bf16* dkrow = reinterpret_cast<bf16*>(a.dk) + head + (size_t)key * D;
-    bf16* dvrow = reinterpret_cast<bf16*>(a.dv) + head + (size_t)key * D;
+    float* dkrow = a.dk + head + (size_t)key * D;
+    float* dvrow = a.dv + head + (size_t)key * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 k4, v4;
+        f32x4 k4, v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          k4[e] = to_bf16(dk[b][4 * g + e] * a.scale);
-          v4[e] = to_bf16(dv[b][4 * g + e]);
+          k4[e] = dk[b][4 * g + e] * a.scale;
+          v4[e] = dv[b][4 * g + e];
         }
-        *reinterpret_cast<bf16x4*>(dkrow + 32 * b + 8 * g + 4 * h) = k4;
-        *reinterpret_cast<bf16x4*>(dvrow + 32 * b + 8 * g + 4 * h) = v4;
+        *reinterpret_cast<f32x4*>(dkrow + 32 * b + 8 * g + 4 * h) = k4;
+        *reinterpret_cast<f32x4*>(dvrow + 32 * b + 8 * g + 4 * h) = v4;
       }
   }
 }
 
 // ---------------------------------------------------------------------- dQ
+// 4 waves, 32 queries per wave; 64-key tiles of K and V in swizzled LDS
+// tiles (K read row-wise for S^T = K Q^T and column-wise for dQ^T += K^T dS^T).
+#ifndef FA_DQ_BK128
+#define FA_DQ_BK128 64
+#endif
+#ifndef FA_DKDV_WAVES128
+#define FA_DKDV_WAVES128 4
+#endif
+
 template <int D>
 struct DqTile {
-  static constexpr int BQ = 128;    // queries per workgroup (4 waves x 32)
-  static constexpr int BK = 64;     // keys per loop step
-  static constexpr int KP = D + 8;  // LDS row pitch (elements)
+  static constexpr int BQ = 128;  // queries per workgroup (4 waves x 32)
+  static constexpr int BK = D == 128 ? FA_DQ_BK128 : 64;  // keys per loop step
   static constexpr int CH = D / 8;
   static constexpr int LOADS = BK * CH / kThreads;
-  static constexpr int T_ELEMS = BK * KP;
+  static constexpr int T_ELEMS = BK * D;
   static_assert(BK * CH % kThreads == 0, "tile must split evenly");
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
   constexpr int DC = D / 16;
@@ -310,24 +330,29 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int idx = threadIdx.x + kThreads * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      const int k = min(t * T::BK + row, N - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(K + (size_t)k * D + 8 * ch);
-      vreg[i] = *reinterpret_cast<const u32x4*>(V + (size_t)k * D + 8 * ch);
+      const int k = min(t * T::BK + idx / T::CH, N - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(K + (size_t)k * D + 8 * (idx % T::CH));
+      vreg[i] = *reinterpret_cast<const u32x4*>(V + (size_t)k * D + 8 * (idx % T::CH));
     }
   };
   auto store_tile = [&](int stage) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int idx = threadIdx.x + kThreads * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      lds_write16(&tiles[stage][0][row * T::KP + 8 * ch], kreg[i]);
-      lds_write16(&tiles[stage][1][row * T::KP + 8 * ch], vreg[i]);
+      const int off = tile_off<D>(idx / T::CH, idx % T::CH);
+      lds_write16(&tiles[stage][0][off], kreg[i]);
+      lds_write16(&tiles[stage][1][off], vreg[i]);
     }
   };
 
+  const int sw_row = tile_swz<D>(l32);
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
+  const int tq = tr_col >> 3, te = tr_col & 7;
+  auto tr_off = [&](int row, int sw, int b) {
+    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+  };
 
   wait_global_loads();  // Q, dO operands resident before the key loop
   int t = 0;
@@ -351,12 +376,12 @@ void bwd_dq_kernel(BwdArgs a) {
         s[r] = 0.f;
         dp[r] = 0.f;
       }
+      const int rrow = (32 * kb + l32) * D;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const bf16x8 ka = lds_read8(Ks + (32 * kb + l32) * T::KP + 16 * c + 8 * h);
-        const bf16x8 va = lds_read8(Vs + (32 * kb + l32) * T::KP + 16 * c + 8 * h);
-        s = mfma32(ka, qf[c], s);
-        dp = mfma32(va, of[c], dp);
+        const int off = rrow + 8 * ((2 * c + h) ^ sw_row);
+        s = mfma32(lds_read8(Ks + off), qf[c], s);
+        dp = mfma32(lds_read8(Vs + off), of[c], dp);
       }
       // s[r], dp[r]: key k0 + 32kb + 8(r/4) + 4h + r%4, query qrow.
 #pragma unroll
@@ -373,11 +398,11 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int cc = 0; cc < 2; ++cc) {
         const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
                                 dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
-        const int rbase = (32 * kb + 16 * cc + tr_row) * T::KP + tr_col;
+        const int r_lo = 32 * kb + 16 * cc + tr_row;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const bf16x8 ka = cat8(lds_read_tr4(Ks + rbase + 32 * b),
-                                 lds_read_tr4(Ks + rbase + 8 * T::KP + 32 * b));
+          const bf16x8 ka = cat8(lds_read_tr4(Ks + tr_off(r_lo, sw_lo, b)),
+                                 lds_read_tr4(Ks + tr_off(r_lo + 8, sw_hi, b)));
           dq[b] = mfma32(ka, db, dq[b]);
         }
       }
@@ -388,34 +413,42 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 
   if (qrow < N) {
-    bf16* dqrow = reinterpret_cast<bf16*>(a.dq) + head + (size_t)qrow * D;
+    float* dqrow = a.dq + head + (size_t)qrow * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
+        f32x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = to_bf16(dq[b][4 * g + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(dqrow + 32 * b + 8 * g + 4 * h) = v4;
+        for (int e = 0; e < 4; ++e) v4[e] = dq[b][4 * g + e] * a.scale;
+        *reinterpret_cast<f32x4*>(dqrow + 32 * b + 8 * g + 4 * h) = v4;
       }
   }
 }
 
+// dK/dV workgroup size: d=128 needs about 300 registers per lane (one wave
+// per SIMD, 4 waves); d=64 fits two waves per SIMD (8 waves).
+template <int D>
+constexpr int kDkdvWaves = D == 128 ? FA_DKDV_WAVES128 : 8;
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+  using TK = DkdvTile<D, kDkdvWaves<D>>;
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = kThreads / (D / 8);
   const long long g0 = (rows + RPB - 1) / RPB;
-  const long long g1 = (long long)((a.N + DkdvTile<D>::BK - 1) / DkdvTile<D>::BK) * a.B * a.H;
+  const long long g1 = (long long)((a.N + TK::BK - 1) / TK::BK) * a.B * a.H;
   const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
   if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
     return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)g0), dim3(kThreads), 0, s, a, rows);
   if (a.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D>, true>), dim3((unsigned)g1),
+                       dim3(TK::THREADS), 0, s, a);
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D>, false>), dim3((unsigned)g1),
+                       dim3(TK::THREADS), 0, s, a);
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();

@@ -102,6 +102,30 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return r;
 }
 
+// XOR swizzle of a row-major LDS tile with D bf16 per row (no padding),
+// applied to the 16-byte chunk index: chunk q of row r is stored at chunk
+// q ^ swz(r).  With the LDS seen as 64 banks of 4 bytes, it makes both
+// access patterns the kernels use conflict-free:
+//   * 16 consecutive rows reading the same chunk (ds_read_b128 operand rows);
+//   * 4 consecutive rows (first row a multiple of 4) reading 4 consecutive
+//     chunks (first a multiple of 4) -- half a wave of ds_read_b64_tr_b16.
+// D = 128: a row is 16 chunks (256 B); swz(r) = 4(r%4) + (r/4)%4 maps the 16
+// rows of an aligned group to 16 distinct chunks, and 4 aligned rows to 4
+// distinct groups of 4 chunks.  D = 64: two rows share one 256-byte bank
+// line; swz(r) = 4((r/2)%2) + (r/4)%4 does the same per row parity.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// Element offset of (row r, 16-byte chunk q) in a swizzled D-wide tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int q) {
+  return r * D + 8 * (q ^ tile_swz<D>(r));
+}
+
 // Workgroup index -> work item, so that consecutive items stay on one XCD
 // (the hardware deals workgroups to the 8 XCDs round-robin; each XCD has its
 // own L2, and items of one head reuse the same K/V).  Falls back to identity

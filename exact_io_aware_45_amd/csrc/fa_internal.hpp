@@ -28,9 +28,9 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  void* dq;
-  void* dk;
-  void* dv;
+  float* dq;
+  float* dk;
+  float* dv;
   float* delta;  // workspace: D_i = dO_i . O_i, [B][H][N] fp32
   int B, H, N, d;
   float scale;

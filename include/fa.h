@@ -74,23 +74,25 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
 /*
- * Backward pass, bf16 storage, fp32 accumulation.  The probabilities are
- * recomputed tile by tile from Q, K and the saved LSE instead of being stored
- * ("FlashAttention." plate, "Never write the scores": the backward recomputes
- * the scores).  Gradients by the chain rule through P = softmax(S):
+ * Backward pass: bf16 inputs, fp32 accumulation and fp32 gradients.  The
+ * probabilities are recomputed tile by tile from Q, K and the saved LSE
+ * instead of being stored ("FlashAttention." plate, "Never write the scores":
+ * the backward recomputes the scores).  Gradients by the chain rule through
+ * P = softmax(S):
  *   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
  *   dQ = scale dS K,  dK = scale dS^T Q.
  *   q, k, v, o, dout in : bf16 [B][H][N][d]  (o and lse from fa_forward with
  *                         the same q, k, v, scale and causal flag)
  *   lse              in : fp32 [B][H][N]
- *   dq, dk, dv       out: bf16 [B][H][N][d]
+ *   dq, dk, dv       out: fp32 [B][H][N][d] (fp32 so that output rounding does
+ *                         not eat the accuracy of the fp32 accumulation)
  *   workspace        scratch device memory of at least
  *                    fa_backward_workspace_size(B, H, N, d) bytes, owned by
  *                    the caller; its contents on entry do not matter.
  * Deterministic: no atomics; the same inputs give bitwise the same outputs.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                const float* lse, float* dq, float* dk, float* dv, void* workspace,
                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                 void* stream);
 
