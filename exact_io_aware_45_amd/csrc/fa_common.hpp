@@ -49,6 +49,15 @@ __device__ __forceinline__ void lds_write16(bf16* p, u32x4 v) {
   *(FA_LDS u32x4*)(p) = v;
 }
 
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's 16 bytes from `src` land at lds_base + 16 * l.  lds_base must be the
+// same for every lane of the wave.  Completion is tracked by the vector
+// memory counter; a workgroup barrier (which waits for it) publishes the data.
+__device__ __forceinline__ void lds_load16(const bf16* src, bf16* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (FA_LDS void*)lds_base, 16, 0, 0);
+}
+
 // Transposed 8-byte LDS read (see the layout note at the top of the file).
 __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(const_cast<bf16*>(p)));

@@ -13,11 +13,14 @@
 // Memory-Efficient Exact Attention with IO-Awareness", Abstract).
 //
 // Work decomposition (MI355X-specific, not from the pages):
-//   * one workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//     query rows for the whole key loop;
-//   * K and V tiles of BC keys are staged HBM -> registers -> LDS, double
-//     buffered, the next tile's global loads in flight during the current
-//     tile's math;
+//   * one workgroup = 8 waves = 256 query rows of one head (4 waves = 128
+//     rows for block-sparse, one mask row); each wave owns 32 query rows for
+//     the whole key loop;
+//   * K and V tiles of BC keys go HBM -> LDS with direct loads
+//     (global_load_lds_dwordx4, no register round trip), double buffered:
+//     the next tile's loads are in flight during the current tile's math.
+//     The tiles are unpadded with an XOR swizzle of the 16-byte chunks, which
+//     keeps both the K row reads and the V transpose reads conflict-free;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //     wave's Q held in registers), so that every lane owns one query column:
 //     the row max and row sum are in-register plus one cross-half exchange;
@@ -38,31 +41,36 @@ namespace fa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBR = 32 * kWaves;  // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 enum Mode { kDense = 0, kCausal = 1, kSparse = 2, kSparseCausal = 3 };
 
-template <int D, int BC>
+template <int D, int BC, int NW>
 struct FwdTile {
-  static constexpr int KP = D + 8;   // K row pitch in LDS (elements)
-  static constexpr int VP = D + 32;  // V row pitch in LDS (elements)
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BR = 32 * NW;  // query rows per workgroup
   static constexpr int CH = D / 8;   // 16-byte chunks per row
-  static constexpr int LOADS = BC * CH / kThreads;
-  static constexpr int K_ELEMS = BC * KP;
-  static constexpr int V_ELEMS = BC * VP;
+  static constexpr int LOADS = BC * CH / THREADS;  // direct loads per lane per tile
+  static constexpr int K_ELEMS = BC * D;  // unpadded rows, XOR-swizzled chunks
+  static constexpr int V_ELEMS = BC * D;
   static constexpr int LDS_BYTES = 2 * (K_ELEMS + V_ELEMS) * 2;
-  static_assert(BC * CH % kThreads == 0, "tile must split evenly over the workgroup");
+  static_assert(BC * CH % THREADS == 0, "tile must split evenly over the workgroup");
 };
 
-template <int D, int BC, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Waves per SIMD the register budget targets: d=128 needs about 215 VGPRs
+// (two waves per SIMD); d=64 fits in 128 (four waves per SIMD).
+template <int D>
+constexpr int kWavesPerEU = D == 64 ? 4 : 2;
+
+template <int D, int BC, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>, kWavesPerEU<D>)))
 void fwd_bf16_kernel(FwdArgs a) {
-  using T = FwdTile<D, BC>;
+  using T = FwdTile<D, BC, NW>;
+  constexpr int kThreads = T::THREADS;
+  constexpr int kBR = T::BR;
   constexpr bool kIsCausal = (MODE == kCausal || MODE == kSparseCausal);
   constexpr bool kIsSparse = (MODE == kSparse || MODE == kSparseCausal);
   constexpr int NB = BC / 32;  // 32-key blocks per tile
@@ -116,29 +124,24 @@ void fwd_bf16_kernel(FwdArgs a) {
     return t;
   };
 
-  u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      const int key = min(t * BC + row, N - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(K + (size_t)key * D + 8 * ch);
-      vreg[i] = *reinterpret_cast<const u32x4*>(V + (size_t)key * D + 8 * ch);
-    }
-  };
-  auto store_tile = [&](int stage) {
+  // HBM -> LDS without a register round trip (global_load_lds_dwordx4):
+  // lane l of a wave's i-th load fills the 16 bytes at LDS position
+  // p = (i * NW + wave) * 64 + l of the tile, i.e. row p / CH, slot p % CH,
+  // which holds the row's chunk slot ^ swz(row).
+  auto load_tile = [&](int t, int stage) {
     bf16* Ks = smem + stage * T::K_ELEMS;
     bf16* Vs = smem + 2 * T::K_ELEMS + stage * T::V_ELEMS;
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      lds_write16(Ks + row * T::KP + 8 * ch, kreg[i]);
-      lds_write16(Vs + row * T::VP + 8 * ch, vreg[i]);
+      const int base = (i * NW + wave) * 64;
+      const int p = base + lane;
+      const int row = p / T::CH;
+      const int q = (p % T::CH) ^ tile_swz<D>(row);
+      const size_t src = (size_t)min(t * BC + row, N - 1) * D + 8 * q;
+      lds_load16(K + src, Ks + 8 * base);
+      lds_load16(V + src, Vs + 8 * base);
     }
   };
-
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
@@ -150,24 +153,31 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   wait_global_loads();  // Q operands resident before the key loop
   int t = next_tile(0);
-  if (t < tend) {
-    load_tile(t);
-    store_tile(0);
-  }
+  if (t < tend) load_tile(t, 0);
   __syncthreads();
   int stage = 0;
 
-  // Lane-invariant parts of the transpose-read address of V^T.
+  // Lane-invariant parts of the swizzled LDS addresses.  K operand rows:
+  // row 32kb + l32, chunk 2c + h.  V^T transpose reads: rows
+  // 32kb + 16cc + tr_row (+8), chunk 4b + (tr_col >> 3), element tr_col & 7.
+  const int sw_row = tile_swz<D>(l32);
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
+  const int tq = tr_col >> 3, te = tr_col & 7;
+  auto tr_off = [&](int row, int sw, int b) {
+    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+  };
 
   while (t < tend) {
     const int tn = next_tile(t + 1);
-    if (tn < tend) load_tile(tn);
+    if (tn < tend) load_tile(tn, stage ^ 1);  // lands during this tile's math
 
     const bf16* Ks = smem + stage * T::K_ELEMS;
     const bf16* Vs = smem + 2 * T::K_ELEMS + stage * T::V_ELEMS;
     const int k0 = t * BC;
+    // A causal tile entirely above this wave's rows contributes nothing.
+    if (!kIsCausal || k0 <= q0 + 32 * wave + 31) {
 
     // S^T = K Q^T for this tile: s[kb] holds keys k0 + 32kb + 8(r/4) + 4h + r%4
     // of query qrow.
@@ -178,7 +188,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const bf16x8 ka = lds_read8(Ks + (32 * kb + l32) * T::KP + 16 * c + 8 * h);
+        const bf16x8 ka = lds_read8(Ks + (32 * kb + l32) * D + 8 * ((2 * c + h) ^ sw_row));
         s[kb] = mfma32(ka, qf[c], s[kb]);
       }
     }
@@ -230,17 +240,17 @@ void fwd_bf16_kernel(FwdArgs a) {
         const bf16x8 pb = pack8(s[kb][8 * cc + 0], s[kb][8 * cc + 1], s[kb][8 * cc + 2],
                                 s[kb][8 * cc + 3], s[kb][8 * cc + 4], s[kb][8 * cc + 5],
                                 s[kb][8 * cc + 6], s[kb][8 * cc + 7]);
-        const bf16* vrow = Vs + (32 * kb + 16 * cc + tr_row) * T::VP + tr_col;
+        const int r_lo = 32 * kb + 16 * cc + tr_row;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const bf16x4 lo = lds_read_tr4(vrow + 32 * b);
-          const bf16x4 hi = lds_read_tr4(vrow + 8 * T::VP + 32 * b);
+          const bf16x4 lo = lds_read_tr4(Vs + tr_off(r_lo, sw_lo, b));
+          const bf16x4 hi = lds_read_tr4(Vs + tr_off(r_lo + 8, sw_hi, b));
           oacc[b] = mfma32(cat8(lo, hi), pb, oacc[b]);
         }
       }
+    }
 
-    if (tn < tend) store_tile(stage ^ 1);
-    __syncthreads();
+    __syncthreads();  // also drains this wave's direct loads of tile tn
     stage ^= 1;
     t = tn;
   }
@@ -265,24 +275,32 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int BC, int MODE>
+template <int D, int BC, int NW, int MODE>
 hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
-  const int nq = (a.N + kBR - 1) / kBR;
+  using T = FwdTile<D, BC, NW>;
+  const int nq = (a.N + T::BR - 1) / T::BR;
   const long long grid = (long long)nq * a.B * a.H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, MODE>), dim3((unsigned)grid), dim3(T::THREADS),
+                     0, s, a);
   return hipGetLastError();
 }
 
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 8
+#endif
+
+// Dense and causal: FA_FWD_WAVES waves (32 query rows each) share every
+// staged K/V tile.  Block-sparse: 4 waves, so that one workgroup covers
+// exactly one 128-row mask row.
 template <int D, int BC>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   if (a.mask) {
-    if (a.causal) return launch_one<D, BC, kSparseCausal>(a, s);
-    return launch_one<D, BC, kSparse>(a, s);
+    if (a.causal) return launch_one<D, BC, 4, kSparseCausal>(a, s);
+    return launch_one<D, BC, 4, kSparse>(a, s);
   }
-  if (a.causal) return launch_one<D, BC, kCausal>(a, s);
-  return launch_one<D, BC, kDense>(a, s);
+  if (a.causal) return launch_one<D, BC, FA_FWD_WAVES, kCausal>(a, s);
+  return launch_one<D, BC, FA_FWD_WAVES, kDense>(a, s);
 }
 
 }  // namespace
