@@ -63,13 +63,19 @@ struct DkdvTile {
   static constexpr int BK = 32 * NW;  // keys per workgroup
   static constexpr int BQ = 64;       // queries per loop step
   static constexpr int CH = D / 8;
-  static constexpr int LOADS = BQ * CH / THREADS;
+  static constexpr int LOADS = BQ * CH / THREADS;  // direct loads per lane per tensor
   static constexpr int T_ELEMS = BQ * D;  // one tile (Q or dO), unpadded
   static_assert(BQ * CH % THREADS == 0, "tile must split evenly");
 };
 
+// d=128 keeps fp32 dK/dV accumulators (128 registers) and the K/V operands
+// (64) resident: one wave per SIMD.  d=64 fits two.
+template <int D>
+constexpr int kDkdvWavesPerEU = D == 128 ? 1 : 2;
+
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(kDkdvWavesPerEU<D>, kDkdvWavesPerEU<D>)))
 void bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D, NW>;
   constexpr int DC = D / 16;
@@ -124,33 +130,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int qt_begin = CAUSAL ? kt0 / T::BQ : 0;
   const float sl2 = a.scale * kLog2e;
 
-  u32x4 qreg[T::LOADS], oreg[T::LOADS];
-  float lreg = 0.f;
-  auto load_tile = [&](int qt) {
+  // HBM -> LDS direct loads of one 64-query tile of Q and dO (swizzled, as
+  // tile_off lays it out) plus its LSE and D rows.
+  auto load_tile = [&](int qt, int st) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + T::THREADS * i;
-      const int q = min(qt * T::BQ + idx / T::CH, N - 1);
-      qreg[i] = *reinterpret_cast<const u32x4*>(Q + (size_t)q * D + 8 * (idx % T::CH));
-      oreg[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)q * D + 8 * (idx % T::CH));
+      const int base = (i * NW + wave) * 64;
+      const int p = base + lane;
+      const int row = p / T::CH;
+      const int q = (p % T::CH) ^ tile_swz<D>(row);
+      const size_t src = (size_t)min(qt * T::BQ + row, N - 1) * D + 8 * q;
+      lds_load16(Q + src, &tiles[st][0][8 * base]);
+      lds_load16(dO + src, &tiles[st][1][8 * base]);
     }
-    if (threadIdx.x < 2 * T::BQ) {
-      const int q = min(qt * T::BQ + (threadIdx.x % T::BQ), N - 1);
-      lreg = threadIdx.x < T::BQ ? LSE[q] * kLog2e : DEL[q];
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + T::THREADS * i;
-      const int off = tile_off<D>(idx / T::CH, idx % T::CH);
-      lds_write16(&tiles[stage][0][off], qreg[i]);
-      lds_write16(&tiles[stage][1][off], oreg[i]);
-    }
-    if (threadIdx.x < T::BQ)
-      lse_s[stage][threadIdx.x] = lreg;
-    else if (threadIdx.x < 2 * T::BQ)
-      del_s[stage][threadIdx.x - T::BQ] = lreg;
+    const int qr = min(qt * T::BQ + lane, N - 1);
+    if (wave == 0) lds_load4(LSE + qr, &lse_s[st][0]);
+    if (wave == 1) lds_load4(DEL + qr, &del_s[st][0]);
   };
 
   // Per-lane swizzle terms.  Row-wise operand reads: row 32qb + l32, chunk
@@ -167,14 +162,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   wait_global_loads();  // K, V operands resident before the query loop
   int qt = qt_begin;
-  if (qt < nqt) {
-    load_tile(qt);
-    store_tile(0);
-  }
+  if (qt < nqt) load_tile(qt, 0);
   __syncthreads();
   int stage = 0;
   for (; qt < nqt; ++qt) {
-    if (qt + 1 < nqt) load_tile(qt + 1);
+    if (qt + 1 < nqt) load_tile(qt + 1, stage ^ 1);  // lands during this tile's math
     const bf16* Qs = tiles[stage][0];
     const bf16* Os = tiles[stage][1];
     const int q0 = qt * T::BQ;
@@ -195,6 +187,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
         s = mfma32(lds_read8(Qs + off), kf[c], s);
         dp = mfma32(lds_read8(Os + off), vf[c], dp);
       }
+      // Issue order: operand reads two MFMAs ahead (one wave per SIMD leaves
+      // nothing else to hide LDS latency behind).
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DC - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       // s[r], dp[r]: query 32qb + 8(r/4) + 4h + r%4 of this tile, key `key`.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -204,7 +205,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
+          float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
           if (need_mask) {
             const int q = q0 + ql + e;
             if (q >= N || (CAUSAL && key > q)) p = 0.f;
@@ -228,9 +229,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dk[b] = mfma32(cat8(lds_read_tr4(Qs + o_lo), lds_read_tr4(Qs + o_hi)), db, dk[b]);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DB - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    if (qt + 1 < nqt) store_tile(stage ^ 1);
-    __syncthreads();
+    __syncthreads();  // also drains this wave's direct loads of the next tile
     stage ^= 1;
   }
 

@@ -58,6 +58,13 @@ __device__ __forceinline__ void lds_load16(const bf16* src, bf16* lds_base) {
                                    (FA_LDS void*)lds_base, 16, 0, 0);
 }
 
+// Direct HBM -> LDS copy of 4 bytes per lane (lane l's value lands at
+// lds_base + 4 * l); same rules as lds_load16.
+__device__ __forceinline__ void lds_load4(const float* src, float* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (FA_LDS void*)lds_base, 4, 0, 0);
+}
+
 // Transposed 8-byte LDS read (see the layout note at the top of the file).
 __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(const_cast<bf16*>(p)));
