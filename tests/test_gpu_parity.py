@@ -97,7 +97,7 @@ def test_forward_f32_single_head_workload():
 def test_forward_full_workloads(name):
     need_gpu()
     w = inputs.WORKLOADS[name]
-    for seed in (0, 1):
+    for seed in (0, 1, 2):
         log(f"{name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal})")
         x = inputs.workload_inputs(w, seed)
         forward_parity(x["q"], x["k"], x["v"], w.causal, sample_pairs(w.B, w.H, 4, seed))
@@ -165,11 +165,20 @@ def test_backward_small(N, d, causal):
 def test_backward_full_workload():
     need_gpu()
     w = inputs.WORKLOADS["bwd_d128_causal"]
-    for seed in (0, 1):
+    for seed in (0, 1, 2):
         log(f"{w.name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal})")
         x = inputs.workload_inputs(w, seed)
         backward_parity(x["q"], x["k"], x["v"], x["dout"], w.causal,
                         sample_pairs(w.B, w.H, 4, seed))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_batched_d64(causal):
+    """d=64 backward at the batched shape (B8 H16 N1024), sampled heads."""
+    need_gpu()
+    log(f"backward B8 H16 N1024 d64 causal={causal}")
+    q, k, v, do = inputs.qkv(8, 16, 1024, 64, torch.bfloat16, seed=5, with_dout=True)
+    backward_parity(q, k, v, do, causal, sample_pairs(8, 16, 6, 5))
 
 
 def test_backward_is_deterministic():
@@ -202,13 +211,15 @@ def test_blocksparse_small(N, d, causal):
     forward_parity(q, k, v, causal, all_pairs(q), mask=mask)
 
 
-def test_blocksparse_full_workload():
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_full_workload(causal):
     need_gpu()
     w = inputs.WORKLOADS["blocksparse_d64"]
-    for seed in (0, 1):
+    for seed in ((0, 1, 2) if not causal else (0,)):
         x = inputs.workload_inputs(w, seed)
-        log(f"{w.name} seed {seed}: {int(x['mask'].sum())} of {x['mask'].numel()} tiles")
-        forward_parity(x["q"], x["k"], x["v"], w.causal, sample_pairs(w.B, w.H, 4, seed),
+        log(f"{w.name} seed {seed} causal={causal}: {int(x['mask'].sum())} of "
+            f"{x['mask'].numel()} tiles")
+        forward_parity(x["q"], x["k"], x["v"], causal, sample_pairs(w.B, w.H, 4, seed),
                        mask=x["mask"])
 
 
