@@ -1,5 +1,6 @@
 """Exact attention for AMD MI355X (gfx950): FlashAttention-style tiled forward,
-backward with recomputation, and block-sparse forward, as hand-written HIP
+backward with recomputation, block-sparse forward and backward, and grouped
+(multi-query / grouped-query) K/V heads, as hand-written HIP
 kernels behind a C ABI (include/fa.h, libfa.so).
 
     from exact_io_aware_45_amd import forward, backward, forward_blocksparse
@@ -8,8 +9,10 @@ kernels behind a C ABI (include/fa.h, libfa.so).
 
 The library is loaded lazily on the first call; a missing libfa.so raises.
 """
-from ._lib import (FAError, backward, backward_workspace_size, error_string, forward,  # noqa: F401
-                   forward_blocksparse, load, runtime_version, version)
+from ._lib import (FAError, backward, backward_blocksparse, backward_gqa,  # noqa: F401
+                   backward_workspace_size, error_string, forward, forward_blocksparse,
+                   forward_gqa, load, runtime_version, version)
 
-__all__ = ["forward", "backward", "forward_blocksparse", "backward_workspace_size",
-           "error_string", "version", "runtime_version", "load", "FAError"]
+__all__ = ["forward", "backward", "forward_blocksparse", "backward_blocksparse", "forward_gqa",
+           "backward_gqa", "backward_workspace_size", "error_string", "version",
+           "runtime_version", "load", "FAError"]

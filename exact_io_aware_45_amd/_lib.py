@@ -18,7 +18,8 @@ LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 SYMBOLS = ("fa_forward", "fa_forward_f32", "fa_backward_workspace_size", "fa_backward",
-           "fa_forward_blocksparse", "fa_error_string", "fa_version", "fa_runtime_version")
+           "fa_forward_blocksparse", "fa_backward_blocksparse", "fa_forward_gqa",
+           "fa_backward_gqa", "fa_error_string", "fa_version", "fa_runtime_version")
 
 _lib = None
 
@@ -47,7 +48,13 @@ def load():
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i,
+                                            i, f, i, vp, i, vp]
+    lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f,
+                                    i, vp]
     for name in ("fa_forward", "fa_forward_f32", "fa_forward_blocksparse", "fa_backward",
+                 "fa_backward_blocksparse", "fa_forward_gqa", "fa_backward_gqa",
                  "fa_version", "fa_runtime_version"):
         getattr(lib, name).restype = i
     lib.fa_error_string.argtypes = [i]
@@ -83,19 +90,41 @@ def _check(status: int, what: str):
         raise FAError(status, what)
 
 
-def _shape(q, k, v, dtype):
+def _tensor(name, t, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _shape(q, k, v, dtype, grouped: bool = False):
+    """(B, H, Hkv, N, d) of q [B,H,N,d] and k, v [B,Hkv,N,d] (Hkv == H unless grouped)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if t.dtype != dtype:
-            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        _tensor(name, t, dtype)
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, d]")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if not (q.shape == k.shape == v.shape):
+    B, H, N, d = (int(x) for x in q.shape)
+    Hkv = int(k.shape[1])
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if grouped:
+        if (int(k.shape[0]), int(k.shape[2]), int(k.shape[3])) != (B, N, d):
+            raise ValueError("k, v must be [B, Hkv, N, d] with q's B, N and d")
+    elif k.shape != q.shape:
         raise ValueError("q, k, v must have the same shape [B, H, N, d]")
-    return tuple(int(x) for x in q.shape)
+    return B, H, Hkv, N, d
+
+
+def _mask(block_mask, N, mask_block):
+    nb = -(-N // mask_block) if mask_block > 0 else 0
+    if (not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8
+            or not block_mask.is_cuda or tuple(block_mask.shape) != (nb, nb)
+            or not block_mask.is_contiguous()):
+        raise ValueError(f"block_mask must be a contiguous uint8 device tensor [{nb}][{nb}]")
 
 
 def _scale(scale, d):
@@ -106,10 +135,10 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None):
     """fa_forward (bf16) or fa_forward_f32 (fp32). Returns (o, lse)."""
     lib = load()
     if q.dtype == torch.float32:
-        B, H, N, d = _shape(q, k, v, torch.float32)
+        B, H, _, N, d = _shape(q, k, v, torch.float32)
         fn, what = lib.fa_forward_f32, "fa_forward_f32"
     else:
-        B, H, N, d = _shape(q, k, v, torch.bfloat16)
+        B, H, _, N, d = _shape(q, k, v, torch.bfloat16)
         fn, what = lib.fa_forward, "fa_forward"
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -122,11 +151,8 @@ def forward_blocksparse(q, k, v, block_mask, mask_block: int = 128, causal: bool
                         scale: float | None = None):
     """fa_forward_blocksparse: block_mask is a uint8 device tensor [nb][nb]."""
     lib = load()
-    B, H, N, d = _shape(q, k, v, torch.bfloat16)
-    nb = -(-N // mask_block) if mask_block > 0 else 0
-    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda
-            or tuple(block_mask.shape) != (nb, nb) or not block_mask.is_contiguous()):
-        raise ValueError(f"block_mask must be a contiguous uint8 device tensor [{nb}][{nb}]")
+    B, H, _, N, d = _shape(q, k, v, torch.bfloat16)
+    _mask(block_mask, N, mask_block)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check(lib.fa_forward_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
@@ -136,27 +162,70 @@ def forward_blocksparse(q, k, v, block_mask, mask_block: int = 128, causal: bool
     return o, lse
 
 
+def forward_gqa(q, k, v, causal: bool = False, scale: float | None = None):
+    """fa_forward_gqa: q [B,H,N,d], k, v [B,Hkv,N,d] bf16 (Hkv divides H)."""
+    lib = load()
+    B, H, Hkv, N, d = _shape(q, k, v, torch.bfloat16, grouped=True)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib.fa_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                              _scale(scale, d), int(bool(causal)), _stream(q.device)),
+           "fa_forward_gqa")
+    return o, lse
+
+
 def backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load().fa_backward_workspace_size(B, H, N, d))
+
+
+def _backward_args(q, k, v, o, dout, lse, grouped, workspace):
+    B, H, Hkv, N, d = _shape(q, k, v, torch.bfloat16, grouped)
+    _tensor("o", o, torch.bfloat16, q.shape)
+    _tensor("dout", dout, torch.bfloat16, q.shape)
+    _tensor("lse", lse, torch.float32, (B, H, N))
+    ws_bytes = backward_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _tensor("workspace", workspace, torch.uint8)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk, dv = (torch.empty(k.shape, dtype=torch.float32, device=q.device) for _ in range(2))
+    return (B, H, Hkv, N, d), workspace, (dq, dk, dv)
 
 
 def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
              workspace=None):
     """fa_backward: returns (dq, dk, dv), fp32."""
     lib = load()
-    B, H, N, d = _shape(q, k, v, torch.bfloat16)
-    for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bf16 device tensor shaped like q")
-    if (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
-            or not lse.is_cuda):
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, N]")
-    ws_bytes = backward_workspace_size(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    (B, H, _, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, False, workspace)
     _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                           _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d,
+                           _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H, N, d,
                            _scale(scale, d), int(bool(causal)), _stream(q.device)),
            "fa_backward")
+    return dq, dk, dv
+
+
+def backward_blocksparse(q, k, v, o, dout, lse, block_mask, mask_block: int = 128,
+                         causal: bool = False, scale: float | None = None, workspace=None):
+    """fa_backward_blocksparse: the gradients of fa_forward_blocksparse, fp32."""
+    lib = load()
+    (B, H, _, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, False, workspace)
+    _mask(block_mask, N, mask_block)
+    _check(lib.fa_backward_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H,
+                                       N, d, _scale(scale, d), int(bool(causal)),
+                                       _ptr(block_mask), int(mask_block), _stream(q.device)),
+           "fa_backward_blocksparse")
+    return dq, dk, dv
+
+
+def backward_gqa(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+                 workspace=None):
+    """fa_backward_gqa: dq [B,H,N,d]; dk, dv [B,Hkv,N,d] summed over each group, fp32."""
+    lib = load()
+    (B, H, Hkv, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, True, workspace)
+    _check(lib.fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H, Hkv, N,
+                               d, _scale(scale, d), int(bool(causal)), _stream(q.device)),
+           "fa_backward_gqa")
     return dq, dk, dv

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -32,18 +32,62 @@ int tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Grouped K/V heads: Hkv must divide H (checked once the shape is non-empty).
+int check_groups(int H, int Hkv) {
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
 int forward_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                   int H, int N, int d, float scale, int causal, const uint8_t* mask,
+                   int H, int Hkv, int N, int d, float scale, int causal, const uint8_t* mask,
                    int mask_block, bool f32, void* stream) {
   bool empty = false;
   int st = check_shape(B, H, N, d, scale, &empty);
   if (st != FA_OK || empty) return st;
+  if ((st = check_groups(H, Hkv)) != FA_OK) return st;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, mask, mask_block};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, mask, mask_block, Hkv};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // do not report an earlier, unrelated error
   return hip_status(f32 ? fa::launch_fwd_f32(a, s) : fa::launch_fwd_bf16(a, s));
+}
+
+size_t workspace_size(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, 1.0f, &empty) != FA_OK || empty) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+int backward_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                    size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
+                    int causal, const uint8_t* mask, int mask_block, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if ((st = check_groups(H, Hkv)) != FA_OK) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dout) ||
+      !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned(workspace, 4) ||
+      workspace_bytes < workspace_size(B, H, N, d))
+    return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{q,  k,  v,  o,     dout,           lse,  dq,         dk, dv,
+                static_cast<float*>(workspace), B, H, N, d, scale, causal ? 1 : 0,
+                mask, mask_block, Hkv};
+  (void)hipGetLastError();
+  return hip_status(fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// Mask arguments: mask_block is checked first (so a bad block size is
+// reported even for empty shapes), then a non-empty problem needs a mask.
+int check_mask(int B, int H, int N, const uint8_t* block_mask, int mask_block) {
+  if (mask_block != 128) return FA_ERR_UNSUPPORTED;
+  if (B > 0 && H > 0 && N > 0 && block_mask == nullptr) return FA_ERR_INVALID_ARG;
+  return FA_OK;
 }
 
 }  // namespace
@@ -52,12 +96,13 @@ extern "C" {
 
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, void* stream) {
-  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, 0, false, stream);
+  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal, nullptr, 0, false,
+                        stream);
 }
 
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                    int H, int N, int d, float scale, int causal, void* stream) {
-  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, nullptr, 0, true, stream);
+  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal, nullptr, 0, true, stream);
 }
 
 int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -66,38 +111,50 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
   bool empty = false;
   int st = check_shape(B, H, N, d, scale, &empty);
   if (st != FA_OK) return st;
-  if (mask_block != 128) return FA_ERR_UNSUPPORTED;
-  if (empty) return FA_OK;
-  if (block_mask == nullptr) return FA_ERR_INVALID_ARG;
-  return forward_common(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, mask_block, false,
+  if ((st = check_mask(B, H, N, block_mask, mask_block)) != FA_OK) return st;
+  return forward_common(q, k, v, o, lse, B, H, H, N, d, scale, causal, block_mask, mask_block,
+                        false, stream);
+}
+
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Hkv, int N, int d, float scale, int causal, void* stream) {
+  if (Hkv < 0) return FA_ERR_INVALID_ARG;
+  return forward_common(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, nullptr, 0, false,
                         stream);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
-  bool empty = false;
-  if (check_shape(B, H, N, d, 1.0f, &empty) != FA_OK || empty) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return (rows * sizeof(float) + 255) / 256 * 256;
+  return workspace_size(B, H, N, d);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                 const float* lse, float* dq, float* dk, float* dv, void* workspace,
                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                 void* stream) {
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H,
+                         N, d, scale, causal, nullptr, 0, stream);
+}
+
+int fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                            float scale, int causal, const uint8_t* block_mask, int mask_block,
+                            void* stream) {
   bool empty = false;
   int st = check_shape(B, H, N, d, scale, &empty);
-  if (st != FA_OK || empty) return st;
-  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dout) ||
-      !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv))
-    return FA_ERR_INVALID_ARG;
-  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  if (workspace == nullptr || !aligned(workspace, 4) ||
-      workspace_bytes < fa_backward_workspace_size(B, H, N, d))
-    return FA_ERR_INVALID_ARG;
-  fa::BwdArgs a{q,  k,  v,  o,  dout, lse,   dq,        dk, dv, static_cast<float*>(workspace),
-                B,  H,  N,  d,  scale, causal ? 1 : 0};
-  (void)hipGetLastError();
-  return hip_status(fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
+  if (st != FA_OK) return st;
+  if ((st = check_mask(B, H, N, block_mask, mask_block)) != FA_OK) return st;
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H,
+                         N, d, scale, causal, block_mask, mask_block, stream);
+}
+
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                    size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
+                    int causal, void* stream) {
+  if (Hkv < 0) return FA_ERR_INVALID_ARG;
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                         Hkv, N, d, scale, causal, nullptr, 0, stream);
 }
 
 const char* fa_error_string(int status) {

@@ -11,6 +11,12 @@
 // to half a bf16 ulp (2^-6 for values in [4, 8), 2^-5 above 8), which is
 // most of the 2e-2 absolute error budget the results are checked against.
 //
+// Grouped K/V heads (Hkv divides H; query head h reads K/V head h / (H/Hkv)):
+// the gradient of a shared K/V head is the sum over the query heads that
+// read it, accumulated inside one workgroup (the dK/dV workgroup loops over
+// the group), so it stays deterministic.  A tile mask skips whole tiles in
+// both passes: the dQ pass walks its mask row, the dK/dV pass its mask column.
+//
 // Three launches on the caller's stream, deterministic (no atomics):
 //   1. bwd_delta: D_i = dO_i . O_i (fp32), into the caller's workspace;
 //   2. bwd_dkdv:  one workgroup per 256 keys; each wave keeps 32 keys' K and V
@@ -31,6 +37,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Template modes: bit 0 = causal, bit 1 = tile mask.
+enum Mode { kDense = 0, kCausal = 1, kSparse = 2, kSparseCausal = 3 };
 
 // ---------------------------------------------------------------- D = dO.O
 template <int D>
@@ -73,11 +82,13 @@ struct DkdvTile {
 template <int D>
 constexpr int kDkdvWavesPerEU = D == 128 ? 1 : 2;
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerEU<D>, kDkdvWavesPerEU<D>)))
 void bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D, NW>;
+  constexpr bool CAUSAL = (MODE & kCausal) != 0;
+  constexpr bool SPARSE = (MODE & kSparse) != 0;
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = T::BQ / 32;
@@ -88,24 +99,27 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nkt = (N + T::BK - 1) / T::BK;
-  const int total = nkt * a.B * a.H;
+  const int total = nkt * a.B * a.Hkv;
   const int w = xcd_remap(blockIdx.x, total);
-  const int bh = w / nkt;
-  const int kt = w % nkt;  // small key tiles see the most queries: first
+  const int bkv = w / nkt;  // K/V head b * Hkv + hk
+  const int kt = w % nkt;   // small key tiles see the most queries: first
   const int kt0 = kt * T::BK;
+  const int G = a.H / a.Hkv;  // query heads per K/V head
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * G;  // the group's first query head
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const size_t head = (size_t)bh * N * D;
-  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + head;
+  const size_t head = (size_t)bkv * N * D;
+  const size_t qhead = (size_t)bq0 * N * D;
+  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + qhead;
   const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
   const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
-  const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + head;
-  const float* __restrict__ LSE = a.lse + (size_t)bh * N;
-  const float* __restrict__ DEL = a.delta + (size_t)bh * N;
+  const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + qhead;
+  const float* __restrict__ LSE = a.lse + (size_t)bq0 * N;
+  const float* __restrict__ DEL = a.delta + (size_t)bq0 * N;
 
   // This wave's keys as B operands: K^T for S = Q K^T, V^T for dP = dO V^T.
   const int key = kt0 + 32 * wave + l32;
@@ -127,23 +141,53 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
 
   const int nqt = (N + T::BQ - 1) / T::BQ;
-  const int qt_begin = CAUSAL ? kt0 / T::BQ : 0;
+  const int qt_begin = CAUSAL ? kt0 / T::BQ : 0;  // < nqt, since kt0 < N
   const float sl2 = a.scale * kLog2e;
+
+  // The (query head g of the group, query tile qt) pairs this workgroup
+  // visits, in order; with a tile mask, pairs whose mask entry
+  // [qt * BQ / mb][kt0 / mb] is 0 are skipped (BK divides mb).
+  const uint8_t* mcol = nullptr;
+  int mb = 1, nmb = 1;
+  if constexpr (SPARSE) {
+    mb = a.mask_block;
+    nmb = (N + mb - 1) / mb;
+    mcol = a.mask + kt0 / mb;
+  }
+  struct Pos {
+    int g, qt;
+  };
+  auto advance = [&](Pos p) {  // the first visited pair at or after p
+    for (;;) {
+      if (p.qt >= nqt) {
+        p.qt = qt_begin;
+        ++p.g;
+      }
+      if (p.g >= G) return p;
+      if constexpr (SPARSE) {
+        if (mcol[(size_t)((p.qt * T::BQ) / mb) * nmb]) return p;
+        ++p.qt;
+      } else {
+        return p;
+      }
+    }
+  };
 
   // HBM -> LDS direct loads of one 64-query tile of Q and dO (swizzled, as
   // tile_off lays it out) plus its LSE and D rows.
-  auto load_tile = [&](int qt, int st) {
+  auto load_tile = [&](Pos p, int st) {
+    const size_t ho = (size_t)p.g * N * D;
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int base = (i * NW + wave) * 64;
-      const int p = base + lane;
-      const int row = p / T::CH;
-      const int q = (p % T::CH) ^ tile_swz<D>(row);
-      const size_t src = (size_t)min(qt * T::BQ + row, N - 1) * D + 8 * q;
+      const int lp = base + lane;
+      const int row = lp / T::CH;
+      const int q = (lp % T::CH) ^ tile_swz<D>(row);
+      const size_t src = ho + (size_t)min(p.qt * T::BQ + row, N - 1) * D + 8 * q;
       lds_load16(Q + src, &tiles[st][0][8 * base]);
       lds_load16(dO + src, &tiles[st][1][8 * base]);
     }
-    const int qr = min(qt * T::BQ + lane, N - 1);
+    const size_t qr = (size_t)p.g * N + min(p.qt * T::BQ + lane, N - 1);
     if (wave == 0) lds_load4(LSE + qr, &lse_s[st][0]);
     if (wave == 1) lds_load4(DEL + qr, &del_s[st][0]);
   };
@@ -161,15 +205,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   wait_global_loads();  // K, V operands resident before the query loop
-  int qt = qt_begin;
-  if (qt < nqt) load_tile(qt, 0);
+  Pos cur = advance(Pos{0, qt_begin});
+  if (cur.g < G) load_tile(cur, 0);
   __syncthreads();
   int stage = 0;
-  for (; qt < nqt; ++qt) {
-    if (qt + 1 < nqt) load_tile(qt + 1, stage ^ 1);  // lands during this tile's math
+  while (cur.g < G) {
+    const Pos nxt = advance(Pos{cur.g, cur.qt + 1});
+    if (nxt.g < G) load_tile(nxt, stage ^ 1);  // lands during this tile's math
     const bf16* Qs = tiles[stage][0];
     const bf16* Os = tiles[stage][1];
-    const int q0 = qt * T::BQ;
+    const int q0 = cur.qt * T::BQ;
     const bool need_mask = (CAUSAL && q0 < kt0 + 32 * wave + 31) || (q0 + T::BQ > N);
 
 #pragma unroll
@@ -239,6 +284,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
     __syncthreads();  // also drains this wave's direct loads of the next tile
     stage ^= 1;
+    cur = nxt;
   }
 
   // dK^T, dV^T (fp32 out): lane holds key `key`, d = 32b + 8(r/4) + 4h + r%4.
@@ -281,10 +327,12 @@ struct DqTile {
   static_assert(BK * CH % kThreads == 0, "tile must split evenly");
 };
 
-template <int D, bool CAUSAL>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
+  constexpr bool CAUSAL = (MODE & kCausal) != 0;
+  constexpr bool SPARSE = (MODE & kSparse) != 0;
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
   constexpr int NB = T::BK / 32;
@@ -305,9 +353,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const int l32 = lane & 31;
 
   const size_t head = (size_t)bh * N * D;
+  const int bkv = (bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv);
+  const size_t kvhead = (size_t)bkv * N * D;
   const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + head;
-  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
-  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
+  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + kvhead;
+  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + kvhead;
   const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + head;
 
   const int qrow = q0 + 32 * wave + l32;
@@ -331,6 +381,20 @@ void bwd_dq_kernel(BwdArgs a) {
   const int nt = (N + T::BK - 1) / T::BK;
   const int qmax = min(q0 + T::BQ, N) - 1;
   const int tend = CAUSAL ? min(nt, qmax / T::BK + 1) : nt;
+  // With a tile mask, key tiles whose entry in this workgroup's mask row is 0
+  // are skipped (BQ equals the mask tile, BK divides it).
+  const uint8_t* mrow = nullptr;
+  int mb = 1;
+  if constexpr (SPARSE) {
+    mb = a.mask_block;
+    mrow = a.mask + (size_t)(q0 / mb) * ((N + mb - 1) / mb);
+  }
+  auto next_tile = [&](int t) {
+    if constexpr (SPARSE) {
+      while (t < tend && !mrow[(t * T::BK) / mb]) ++t;
+    }
+    return t;
+  };
 
   u32x4 kreg[T::LOADS], vreg[T::LOADS];
   auto load_tile = [&](int t) {
@@ -362,15 +426,16 @@ void bwd_dq_kernel(BwdArgs a) {
   };
 
   wait_global_loads();  // Q, dO operands resident before the key loop
-  int t = 0;
+  int t = next_tile(0);
   if (t < tend) {
     load_tile(t);
     store_tile(0);
   }
   __syncthreads();
   int stage = 0;
-  for (; t < tend; ++t) {
-    if (t + 1 < tend) load_tile(t + 1);
+  while (t < tend) {
+    const int tn = next_tile(t + 1);
+    if (tn < tend) load_tile(tn);
     const bf16* Ks = tiles[stage][0];
     const bf16* Vs = tiles[stage][1];
     const int k0 = t * T::BK;
@@ -414,9 +479,10 @@ void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    if (t + 1 < tend) store_tile(stage ^ 1);
+    if (tn < tend) store_tile(stage ^ 1);
     __syncthreads();
     stage ^= 1;
+    t = tn;
   }
 
   if (qrow < N) {
@@ -434,31 +500,37 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 // dK/dV workgroup size: d=128 needs about 300 registers per lane (one wave
-// per SIMD, 4 waves); d=64 fits two waves per SIMD (8 waves).
-template <int D>
-constexpr int kDkdvWaves = D == 128 ? FA_DKDV_WAVES128 : 8;
+// per SIMD, 4 waves); d=64 fits two waves per SIMD (8 waves).  With a tile
+// mask the workgroup's 32 * NW keys must lie in one mask column: 4 waves.
+template <int D, int MODE>
+constexpr int kDkdvWaves = (MODE & kSparse) ? 4 : (D == 128 ? FA_DKDV_WAVES128 : 8);
+
+template <int D, int MODE>
+hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
+  using TK = DkdvTile<D, kDkdvWaves<D, MODE>>;
+  static_assert(!(MODE & kSparse) || 128 % TK::BK == 0, "dK/dV keys must fit one mask tile");
+  static_assert(!(MODE & kSparse) || DqTile<D>::BQ == 128, "dQ rows must be one mask tile");
+  const long long g1 = (long long)((a.N + TK::BK - 1) / TK::BK) * a.B * a.Hkv;
+  const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D, MODE>, MODE>), dim3((unsigned)g1),
+                     dim3(TK::THREADS), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
-  using TK = DkdvTile<D, kDkdvWaves<D>>;
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = kThreads / (D / 8);
   const long long g0 = (rows + RPB - 1) / RPB;
-  const long long g1 = (long long)((a.N + TK::BK - 1) / TK::BK) * a.B * a.H;
-  const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
-  if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
-    return hipErrorInvalidConfiguration;
+  if (g0 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.mask && a.mask_block != 128) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)g0), dim3(kThreads), 0, s, a, rows);
-  if (a.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D>, true>), dim3((unsigned)g1),
-                       dim3(TK::THREADS), 0, s, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D>, false>), dim3((unsigned)g1),
-                       dim3(TK::THREADS), 0, s, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
-  }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.mask) return a.causal ? launch_mode<D, kSparseCausal>(a, s) : launch_mode<D, kSparse>(a, s);
+  return a.causal ? launch_mode<D, kCausal>(a, s) : launch_mode<D, kDense>(a, s);
 }
 
 }  // namespace

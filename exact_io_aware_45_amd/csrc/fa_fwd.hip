@@ -92,10 +92,13 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
+  // Query head bh = b * H + hq reads K/V head b * Hkv + hq / (H / Hkv).
   const size_t head = (size_t)bh * (size_t)N * D;
+  const int bkv = (bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv);
+  const size_t kvhead = (size_t)bkv * (size_t)N * D;
   const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + head;
-  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
-  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
+  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + kvhead;
+  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + kvhead;
   bf16* __restrict__ O = reinterpret_cast<bf16*>(a.o) + head;
 
   // Q^T operand of this wave: query row qrow, d = 16c + 8h .. +7.

@@ -6,8 +6,9 @@
 
 namespace fa {
 
-// Problem description shared by every forward launch.  Tensors are contiguous
-// [B][H][N][d]; lse is [B][H][N] fp32.
+// Problem description shared by every forward launch.  Q, O are contiguous
+// [B][H][N][d], K, V [B][Hkv][N][d] (Hkv divides H; query head h reads K/V
+// head h / (H / Hkv)); lse is [B][H][N] fp32.
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -19,6 +20,7 @@ struct FwdArgs {
   int causal;
   const uint8_t* mask;  // tile mask [nmb][nmb] or nullptr
   int mask_block;       // tile edge of the mask (keys and queries)
+  int Hkv;
 };
 
 struct BwdArgs {
@@ -35,6 +37,9 @@ struct BwdArgs {
   int B, H, N, d;
   float scale;
   int causal;
+  const uint8_t* mask;  // tile mask [nmb][nmb] or nullptr
+  int mask_block;
+  int Hkv;  // K, V, dK, dV are [B][Hkv][N][d]; dK/dV sum over the H/Hkv query heads
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

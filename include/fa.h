@@ -12,7 +12,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  Layout     Q, K, V, O, dO, dQ, dK, dV are dense, contiguous [B][H][N][d]
- *             tensors (row-major, d fastest).  LSE is [B][H][N] fp32, the
+ *             tensors (row-major, d fastest); the _gqa entry points take K,
+ *             V, dK, dV as [B][Hkv][N][d].  LSE is [B][H][N] fp32, the
  *             natural-log log-sum-exp of row i of the scaled, masked scores.
  *  Memory     every tensor pointer is a DEVICE pointer on the current HIP
  *             device; `block_mask` is a device pointer too.  The caller owns
@@ -112,6 +113,49 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, int causal,
                            const uint8_t* block_mask, int mask_block, void* stream);
+
+/*
+ * Block-sparse backward: the gradients of fa_forward_blocksparse with the same
+ * mask.  Tiles whose mask entry is 0 are skipped in both gradient passes (the
+ * dQ pass walks each mask row, the dK/dV pass each mask column), so masked
+ * tiles cost no loads and no matrix work here either ("Flash Attention:
+ * IO-Aware Attention Computation", paragraph on block-sparse attention).
+ * Arguments as fa_backward, plus block_mask / mask_block as
+ * fa_forward_blocksparse; o and lse must come from fa_forward_blocksparse
+ * with the same mask.  Rows whose mask row is all zero get dQ = 0, and keys
+ * whose mask column is all zero get dK = dV = 0.
+ */
+int fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                            float scale, int causal, const uint8_t* block_mask, int mask_block,
+                            void* stream);
+
+/*
+ * Grouped K/V heads (multi-query attention for Hkv = 1, grouped-query
+ * attention for 1 < Hkv < H): "Flash Attention: IO-Aware Attention
+ * Computation", closing paragraph on future directions, names these variants
+ * as a way to shrink the key/value memory.  Query head h of batch b attends
+ * to K/V head h / (H / Hkv) of batch b; everything else is fa_forward.
+ *   q, o      bf16 [B][H][N][d]      lse fp32 [B][H][N]
+ *   k, v      bf16 [B][Hkv][N][d]    (1 <= Hkv <= H, H % Hkv == 0, else
+ *                                     FA_ERR_INVALID_ARG)
+ * fa_forward_gqa with Hkv == H is fa_forward.
+ */
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Hkv, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * Backward of fa_forward_gqa.  dq is fp32 [B][H][N][d]; dk and dv are fp32
+ * [B][Hkv][N][d]: the gradient of a shared K/V head is the sum, over the
+ * H / Hkv query heads that read it, of each head's gradient.  The sum is
+ * taken inside one workgroup in a fixed order (no atomics): deterministic.
+ * workspace: fa_backward_workspace_size(B, H, N, d) bytes (H = query heads).
+ */
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                    size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
+                    int causal, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* fa_error_string(int status);

@@ -128,3 +128,42 @@ def backward(q, k, v, dout, scale: float, causal: bool = False, block_mask=None,
     if rc != 0:
         raise RuntimeError("oracle_backward failed")
     return dq, dk, dv, lse, delta
+
+
+def _groups(q, k):
+    """Query heads per K/V head for q [..., H, N, d] and k [..., Hkv, N, d]."""
+    if q.ndim < 3 or k.ndim != q.ndim or q.shape[:-3] != k.shape[:-3] or \
+            q.shape[-2:] != k.shape[-2:]:
+        raise ValueError("q must be [..., H, N, d] and k, v [..., Hkv, N, d]")
+    H, Hkv = q.shape[-3], k.shape[-3]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"Hkv={Hkv} must divide H={H}")
+    return H // Hkv
+
+
+def forward_gqa(q, k, v, scale: float, causal: bool = False, threads: int = 0):
+    """Grouped K/V heads: query head h reads K/V head h // (H / Hkv).
+
+    Multi-query and grouped-query attention ("Flash Attention: IO-Aware
+    Attention Computation", closing paragraph on future directions) are plain
+    attention per query head with some K/V heads shared; each query head's
+    result is the plain definition above with its group's K and V.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g = _groups(q, k)
+    return forward(q, np.repeat(k, g, axis=-3), np.repeat(v, g, axis=-3), scale, causal,
+                   threads=threads)
+
+
+def backward_gqa(q, k, v, dout, scale: float, causal: bool = False, threads: int = 0):
+    """dQ [..., H, N, d] and dK, dV [..., Hkv, N, d] of forward_gqa.
+
+    A K/V head read by several query heads is one parameter used several
+    times, so its gradient is the sum of the per-query-head gradients.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    g = _groups(q, k)
+    dq, dk, dv, lse, delta = backward(q, np.repeat(k, g, axis=-3), np.repeat(v, g, axis=-3),
+                                      dout, scale, causal, threads=threads)
+    shape = k.shape[:-3] + (k.shape[-3], g) + k.shape[-2:]
+    return dq, dk.reshape(shape).sum(axis=-3), dv.reshape(shape).sum(axis=-3), lse, delta

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("fa_forward", "fa_backward", "fa_forward_blocksparse"):
+    for n in ("fa_forward", "fa_backward", "fa_forward_blocksparse", "fa_backward_blocksparse",
+              "fa_forward_gqa", "fa_backward_gqa"):
         assert n in names
     assert set(names) == set(_lib.SYMBOLS)
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_error_strings():
     lib = _lib.load()
-    assert _lib.version() == 100
+    assert _lib.version() == 200
     for st in range(4):
         s = _lib.error_string(st)
         assert isinstance(s, str) and s
@@ -123,3 +124,45 @@ def test_backward_workspace_and_argument_errors():
         assert bwd(**{name: None}) == INV, name
     assert bwd(dq=MIS) == INV
     assert bwd(do=MIS) == INV
+
+
+def test_blocksparse_backward_argument_errors():
+    lib = _lib.load()
+    ws = _lib.backward_workspace_size(1, 1, 256, 64)
+
+    def bwd(mask=FAKE, mb=128, N=256, q=FAKE, ws_bytes=ws):
+        return lib.fa_backward_blocksparse(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, ws_bytes, 1, 1, N, 64, 0.125, 0, mask, mb, None)
+
+    assert bwd(mask=None) == _lib.FA_ERR_INVALID_ARG
+    assert bwd(mb=64) == _lib.FA_ERR_UNSUPPORTED
+    assert bwd(mb=64, N=0) == _lib.FA_ERR_UNSUPPORTED
+    assert bwd(q=MIS) == _lib.FA_ERR_INVALID_ARG
+    assert bwd(ws_bytes=ws - 4) == _lib.FA_ERR_INVALID_ARG
+    assert bwd(mask=None, q=None, N=0) == _lib.FA_OK
+
+
+def test_gqa_argument_errors():
+    lib = _lib.load()
+    INV, OK = _lib.FA_ERR_INVALID_ARG, _lib.FA_OK
+
+    def fwd_g(H=8, Hkv=2, N=64, d=64, q=FAKE):
+        return lib.fa_forward_gqa(q, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, N, d, 0.125, 1, None)
+
+    assert fwd_g(Hkv=0) == INV
+    assert fwd_g(Hkv=-1) == INV
+    assert fwd_g(Hkv=3) == INV      # does not divide H
+    assert fwd_g(Hkv=16) == INV     # more K/V heads than query heads
+    assert fwd_g(q=None) == INV
+    assert fwd_g(d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert fwd_g(N=0, q=None) == OK
+    ws = _lib.backward_workspace_size(1, 8, 64, 64)
+
+    def bwd_g(Hkv=2, ws_bytes=ws, dk=FAKE):
+        return lib.fa_backward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dk, FAKE, FAKE,
+                                   ws_bytes, 1, 8, Hkv, 64, 64, 0.125, 0, None)
+
+    assert bwd_g(Hkv=3) == INV
+    assert bwd_g(Hkv=0) == INV
+    assert bwd_g(dk=None) == INV
+    assert bwd_g(ws_bytes=ws - 4) == INV

@@ -237,3 +237,131 @@ def test_blocksparse_mask_identities():
     assert torch.equal(oc, o2) and torch.equal(lc, l2)
     o3, l3 = run_forward(q, k, v, False, mask=torch.zeros(nb, nb, dtype=torch.uint8))
     assert torch.all(o3 == 0) and torch.all(torch.isneginf(l3))
+
+
+def test_blocksparse_two_key_halves_merge_to_the_full_result():
+    """The sequence-sharding combine rule: attention over two disjoint key sets,
+    merged with their LSEs, equals attention over all keys."""
+    need_gpu()
+    N, nb = 1000, 8
+    q, k, v = inputs.qkv(1, 4, N, 128, torch.bfloat16, seed=31)
+    full_o, full_l = run_forward(q, k, v, False)
+    left = torch.zeros(nb, nb, dtype=torch.uint8)
+    left[:, : nb // 2] = 1
+    oa, la = run_forward(q, k, v, False, mask=left)
+    ob, lb = run_forward(q, k, v, False, mask=1 - left)
+    lse = torch.logaddexp(la, lb)
+    o = torch.exp(la - lse)[..., None] * oa.float() + torch.exp(lb - lse)[..., None] * ob.float()
+    assert (o - full_o.float()).abs().max() <= 1e-2
+    assert (lse - full_l).abs().max() <= 1e-5
+
+
+# ------------------------------------------------------ block-sparse backward
+def backward_parity_sparse(q, k, v, do, causal, pairs, mask):
+    qd, kd, vd, dod, md = (t.to(DEV) for t in (q, k, v, do, mask))
+    o, lse = _lib.forward_blocksparse(qd, kd, vd, md, causal=causal)
+    dq, dk, dv = _lib.backward_blocksparse(qd, kd, vd, o, dod, lse, md, causal=causal)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    scale = q.shape[-1] ** -0.5
+    rdq, rdk, rdv, _, _ = oracle.backward(heads_of(q, pairs), heads_of(k, pairs),
+                                          heads_of(v, pairs), heads_of(do, pairs), scale, causal,
+                                          block_mask=mask.numpy(), mask_block=128)
+    for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        check(name, np.stack([to64(g[b, h]) for b, h in pairs]), r)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 300, 700])
+def test_blocksparse_backward_small(N, d, causal):
+    need_gpu()
+    log(f"block-sparse backward B2 H2 N{N} d{d} causal={causal}")
+    q, k, v, do = inputs.qkv(2, 2, N, d, torch.bfloat16, seed=17 * N + d, with_dout=True)
+    nb = -(-N // 128)
+    g = torch.Generator().manual_seed(N + 1)
+    mask = (torch.rand(nb, nb, generator=g) < 0.5).to(torch.uint8)
+    if nb > 2:
+        mask[1, :] = 0  # an empty mask row: dQ = 0
+        mask[:, 2] = 0  # an empty mask column: dK = dV = 0
+    dq, dk, dv = backward_parity_sparse(q, k, v, do, causal, all_pairs(q), mask)
+    if nb > 2:
+        assert torch.all(dq[:, :, 128:256] == 0)
+        assert torch.all(dk[:, :, 256:384] == 0) and torch.all(dv[:, :, 256:384] == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_backward_full_workload(causal):
+    need_gpu()
+    w = inputs.WORKLOADS["blocksparse_d64"]
+    x = inputs.workload_inputs(w, 0)
+    do = inputs.qkv(w.B, w.H, w.N, w.d, torch.bfloat16, seed=0, with_dout=True)[3]
+    log(f"{w.name} backward causal={causal}")
+    backward_parity_sparse(x["q"], x["k"], x["v"], do, causal, sample_pairs(w.B, w.H, 2, 3),
+                           x["mask"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse_backward_mask_identities(d):
+    """All-ones mask = dense and lower-triangular mask + causal = causal, bitwise."""
+    need_gpu()
+    N = 1000
+    nb = -(-N // 128)
+    q, k, v, do = (t.to(DEV) for t in inputs.qkv(1, 3, N, d, torch.bfloat16, seed=23,
+                                                 with_dout=True))
+    for causal, mask in ((False, torch.ones(nb, nb, dtype=torch.uint8)),
+                         (True, torch.ones(nb, nb, dtype=torch.uint8).tril())):
+        o, lse = _lib.forward(q, k, v, causal=causal)
+        dense = _lib.backward(q, k, v, o, do, lse, causal=causal)
+        sparse = _lib.backward_blocksparse(q, k, v, o, do, lse, mask.to(DEV), causal=causal)
+        torch.cuda.synchronize()
+        for a, b in zip(dense, sparse):
+            assert torch.equal(a, b)
+
+
+# ------------------------------------------------------- grouped K/V heads
+def gqa_parity(B, H, Hkv, N, d, causal, seed, backward=True):
+    q, _, _, do = inputs.qkv(B, H, N, d, torch.bfloat16, seed=seed, with_dout=True)
+    _, k, v = inputs.qkv(B, Hkv, N, d, torch.bfloat16, seed=seed + 1)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = _lib.forward_gqa(qd, kd, vd, causal=causal)
+    scale = d ** -0.5
+    ro, rl = oracle.forward_gqa(q, k, v, scale, causal)
+    check("O", to64(o.cpu()), ro)
+    check_lse(lse.cpu(), rl, True)
+    if backward:
+        dq, dk, dv = _lib.backward_gqa(qd, kd, vd, o, dod, lse, causal=causal)
+        rdq, rdk, rdv, _, _ = oracle.backward_gqa(q, k, v, do, scale, causal)
+        for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+            check(name, to64(g.cpu()), r)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv,N", [(4, 2, 65), (4, 1, 200), (6, 3, 333)])
+def test_gqa_small(H, Hkv, N, d, causal):
+    need_gpu()
+    log(f"gqa B2 H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    gqa_parity(2, H, Hkv, N, d, causal, seed=N + H + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_larger(causal):
+    need_gpu()
+    log(f"gqa B1 H8 Hkv2 N1024 d128 causal={causal}")
+    gqa_parity(1, 8, 2, 1024, 128, causal, seed=41)
+
+
+def test_gqa_with_hkv_equal_h_is_plain_attention():
+    need_gpu()
+    q, k, v, do = (t.to(DEV) for t in inputs.qkv(2, 4, 300, 128, torch.bfloat16, seed=43,
+                                                 with_dout=True))
+    o1, l1 = _lib.forward(q, k, v, causal=True)
+    o2, l2 = _lib.forward_gqa(q, k, v, causal=True)
+    g1 = _lib.backward(q, k, v, o1, do, l1, causal=True)
+    g2 = _lib.backward_gqa(q, k, v, o1, do, l1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

@@ -333,3 +333,82 @@ def test_empty_and_argument_errors():
     with pytest.raises(ValueError):
         oracle.forward(np.zeros((9, 4)), np.zeros((9, 4)), np.zeros((9, 4)), 1.0,
                        block_mask=np.ones((2, 2), np.uint8), mask_block=4)
+
+
+# ------------------------------------------------- grouped K/V heads (MQA/GQA)
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (3, 1), (2, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_forward_matches_decimal_brute_force(H, Hkv, causal):
+    """Query head h of a batch reads K/V head h // (H / Hkv) of that batch."""
+    B, N, d = 2, 4, 2
+    q, k, v = rand(B, H, N, d), rand(B, Hkv, N, d), rand(B, Hkv, N, d)
+    o, lse = oracle.forward_gqa(q, k, v, 0.9, causal)
+    assert o.shape == (B, H, N, d) and lse.shape == (B, H, N)
+    vis = (lambda i, j: j <= i) if causal else (lambda i, j: True)
+    for b in range(B):
+        for h in range(H):
+            kv = h // (H // Hkv)
+            ob, lb = brute_decimal(q[b, h], k[b, kv], v[b, kv], 0.9, vis)
+            np.testing.assert_allclose(o[b, h], ob, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[b, h], lb, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (3, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_matches_finite_differences(H, Hkv, causal):
+    """dK, dV of a shared head: derivative of L = sum(dO * O) over every query head."""
+    B, N, d, scale = 1, 5, 2, 0.7
+    q, k, v, do = rand(B, H, N, d), rand(B, Hkv, N, d), rand(B, Hkv, N, d), rand(B, H, N, d)
+    dq, dk, dv, _, _ = oracle.backward_gqa(q, k, v, do, scale, causal)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+
+    def loss(q_, k_, v_):
+        return float(np.sum(do * oracle.forward_gqa(q_, k_, v_, scale, causal)[0]))
+
+    h = 1e-6
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        for idx in np.ndindex(*g.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += h
+            lp = loss(*args)
+            args[which][idx] -= 2 * h
+            lm = loss(*args)
+            assert abs((lp - lm) / (2 * h) - g[idx]) < 1e-6, (which, idx)
+
+
+def test_gqa_backward_matches_torch_autograd_fp64():
+    B, H, Hkv, N, d = 2, 6, 2, 40, 8
+    scale = 1 / math.sqrt(d)
+    q, k, v, do = rand(B, H, N, d), rand(B, Hkv, N, d), rand(B, Hkv, N, d), rand(B, H, N, d)
+    dq, dk, dv, _, _ = oracle.backward_gqa(q, k, v, do, scale, True)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    kk = tk.repeat_interleave(H // Hkv, dim=1)
+    vv = tv.repeat_interleave(H // Hkv, dim=1)
+    o = F.scaled_dot_product_attention(tq, kk, vv, is_causal=True, scale=scale)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_mqa_with_identical_query_heads():
+    """Hkv = 1 and every query head equal: equal outputs, and dK, dV are H times one head's."""
+    H, N, d = 3, 12, 4
+    q1, k, v, do1 = rand(1, 1, N, d), rand(1, 1, N, d), rand(1, 1, N, d), rand(1, 1, N, d)
+    q, do = np.repeat(q1, H, axis=1), np.repeat(do1, H, axis=1)
+    o, lse = oracle.forward_gqa(q, k, v, 0.5, True)
+    o1, lse1 = oracle.forward(q1, k, v, 0.5, True)
+    for h in range(H):
+        np.testing.assert_array_equal(o[:, h], o1[:, 0])
+        np.testing.assert_array_equal(lse[:, h], lse1[:, 0])
+    _, dk, dv, _, _ = oracle.backward_gqa(q, k, v, do, 0.5, True)
+    _, dk1, dv1, _, _ = oracle.backward(q1, k, v, do1, 0.5, True)
+    np.testing.assert_allclose(dk, H * dk1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, H * dv1, rtol=0, atol=1e-13)
+
+
+def test_gqa_shape_errors():
+    with pytest.raises(ValueError):
+        oracle.forward_gqa(rand(1, 4, 3, 2), rand(1, 3, 3, 2), rand(1, 3, 3, 2), 1.0)
+    with pytest.raises(ValueError):
+        oracle.forward_gqa(rand(1, 4, 3, 2), rand(1, 2, 5, 2), rand(1, 2, 5, 2), 1.0)

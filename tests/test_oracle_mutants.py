@@ -191,3 +191,83 @@ def test_mutant_is_caught(name, old, new):
     finally:
         shutil.rmtree(tmp)
     assert failed, f"no pin catches the planted mistake {name}"
+
+
+# ------------------------------------------ grouped K/V heads (oracle/__init__.py)
+PY_MUTANTS = [
+    ("gqa_heads_tiled", "np.repeat(k, g, axis=-3), np.repeat(v, g, axis=-3), scale, causal,\n"
+     "                   threads=threads)",
+     "np.concatenate([k] * g, axis=-3), np.concatenate([v] * g, axis=-3), scale, causal,\n"
+     "                   threads=threads)"),
+    ("gqa_group_sum_transposed", "shape = k.shape[:-3] + (k.shape[-3], g) + k.shape[-2:]\n"
+     "    return dq, dk.reshape(shape).sum(axis=-3), dv.reshape(shape).sum(axis=-3), lse, delta",
+     "shape = k.shape[:-3] + (g, k.shape[-3]) + k.shape[-2:]\n"
+     "    return dq, dk.reshape(shape).sum(axis=-4), dv.reshape(shape).sum(axis=-4), lse, delta"),
+    ("gqa_dk_not_summed", "dk.reshape(shape).sum(axis=-3), dv.reshape",
+     "dk.reshape(shape)[..., 0, :, :], dv.reshape"),
+]
+
+
+def load_oracle_package(init_text, tmp):
+    import importlib.util
+    import sys
+    pkg = os.path.join(tmp, "oracle_mut")
+    os.makedirs(pkg)
+    shutil.copy(SRC, os.path.join(pkg, "oracle.c"))
+    with open(os.path.join(pkg, "__init__.py"), "w") as f:
+        f.write(init_text)
+    spec = importlib.util.spec_from_file_location("oracle_mut", os.path.join(pkg, "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules.pop("oracle_mut", None)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def gqa_pins_fail(orc) -> list:
+    rng = np.random.default_rng(5)
+    failed = []
+    B, H, Hkv, N, d = 1, 4, 2, 4, 2
+    q, do = rng.standard_normal((B, H, N, d)), rng.standard_normal((B, H, N, d))
+    k, v = rng.standard_normal((B, Hkv, N, d)), rng.standard_normal((B, Hkv, N, d))
+    o, _ = orc.forward_gqa(q, k, v, 0.9, True)
+    for h in range(H):
+        ob, _ = brute(q[0, h], k[0, h // 2], v[0, h // 2], 0.9, lambda i, j: j <= i)
+        if not np.allclose(o[0, h], ob, rtol=0, atol=1e-12):
+            failed.append("brute_force")
+            break
+    _, dk, dv, _, _ = orc.backward_gqa(q, k, v, do, 0.9, True)
+    eps, worst = 1e-6, 0.0
+    for which, g in ((1, dk), (2, dv)):
+        for idx in np.ndindex(*g.shape):
+            args = [q, k.copy(), v.copy()]
+            args[which][idx] += eps
+            lp = float(np.sum(do * orc.forward_gqa(*args, 0.9, True)[0]))
+            args[which][idx] -= 2 * eps
+            lm = float(np.sum(do * orc.forward_gqa(*args, 0.9, True)[0]))
+            worst = max(worst, abs((lp - lm) / (2 * eps) - g[idx]))
+    if not worst < 1e-6:
+        failed.append("finite_differences")
+    return failed
+
+
+INIT = os.path.join(ROOT, "oracle", "__init__.py")
+
+
+def test_real_gqa_oracle_passes_its_pins():
+    tmp = tempfile.mkdtemp()
+    try:
+        assert gqa_pins_fail(load_oracle_package(open(INIT).read(), tmp)) == []
+    finally:
+        shutil.rmtree(tmp)
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_gqa_mutant_is_caught(name, old, new):
+    text = open(INIT).read()
+    assert old in text, f"mutation site for {name} not found in oracle/__init__.py"
+    tmp = tempfile.mkdtemp()
+    try:
+        failed = gqa_pins_fail(load_oracle_package(text.replace(old, new, 1), tmp))
+    finally:
+        shutil.rmtree(tmp)
+    assert failed, f"no pin catches the planted mistake {name}"
