@@ -1,19 +1,24 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = fa_forward + fa_backward (the whole forward/backward path) on the
-long causal workload: B=1, H=32, N=8192, d=128, bf16, causal, inputs already
-resident in HBM.  Timing uses HIP events on the stream the kernels run on.
-Prints ONE JSON line:
+Default: one step = fa_forward + fa_backward (the whole forward/backward path)
+on the long causal workload: B=1, H=32, N=8192, d=128, bf16, causal, inputs
+already resident in HBM.  Timing uses HIP events on the stream the kernels run
+on.  Prints ONE JSON line:
   value        whole-step TFLOP/s with the algorithmic FLOP counts
                forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, both halved for causal
+               (block-sparse: 4*d resp. 10*d per visible (query, key) pair)
   fwd / bwd    each pass's own time, TFLOP/s and fraction of the bf16 MFMA peak
   roofline     the forward kernel (one launch per fa_forward) against the bf16
-               dense MFMA peak; the backward call gets the same treatment in
-               roofline_bwd
+               dense MFMA peak, or against HBM bandwidth when its arithmetic
+               intensity is below the ridge point; the backward call gets the
+               same treatment in roofline_bwd
   cpu_baseline the fp64 CPU oracle, timed on this host on a bounded sample of
-               the same workload (whole heads, forward + backward)
+               the same workload (whole heads, the same passes)
+
+--workload runs one of the other named workloads (exact_io_aware_45_amd.inputs)
+with the same line format; forward-only workloads time fa_forward alone.
 """
 from __future__ import annotations
 
@@ -31,15 +36,34 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense; p
 PEAK_HBM_GBS = 8000.0
 
 
-def flops(w, which: str) -> float:
-    base = w.B * w.H * float(w.N) ** 2 * w.d
-    f = {"fwd": 4.0, "bwd": 10.0}[which] * base
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+
+
+def visible_pairs(w, mask) -> float:
+    """(query, key) pairs a block-sparse head computes: sum over set tiles of rows x keys."""
+    import torch
+    nb = mask.shape[0]
+    sizes = torch.tensor([min(w.mask_block, w.N - i * w.mask_block) for i in range(nb)],
+                         dtype=torch.float64)
+    tiles = mask.to(torch.float64) * sizes[:, None] * sizes[None, :]
+    if w.causal:  # diagonal tiles keep their lower triangle, tiles above it nothing
+        on_diag = torch.diagonal(mask).to(torch.float64) * sizes * (sizes + 1) / 2
+        return float(torch.tril(tiles, -1).sum() + on_diag.sum())
+    return float(tiles.sum())
+
+
+def flops(w, which: str, mask=None) -> float:
+    per = {"fwd": 4.0, "bwd": 10.0}[which]
+    if mask is not None:
+        return per * w.B * w.H * w.d * visible_pairs(w, mask)
+    f = per * w.B * w.H * float(w.N) ** 2 * w.d
     return f / 2 if w.causal else f
 
 
 def traffic_bytes(w, which: str) -> float:
     """Algorithmic HBM bytes of one call: read the inputs once, write the outputs once."""
-    t = w.B * w.H * w.N * w.d * 2.0  # one bf16 tensor
+    es = 4.0 if w.dtype == "f32" else 2.0
+    t = w.B * w.H * w.N * w.d * es   # one input-dtype tensor
     rows = w.B * w.H * w.N * 4.0     # one fp32 [B,H,N] vector
     if which == "fwd":
         return 3 * t + t + rows                 # Q K V in, O + LSE out
@@ -72,25 +96,51 @@ def load_traffic(path: str) -> dict:
             if k in t and shas.get(k) == source_sha(files)}
 
 
-def cpu_baseline(w, inp, budget_s: float = 15.0, max_heads: int = 32):
-    """Time the fp64 oracle (forward + backward of whole heads) on the host cores."""
+def cpu_baseline(w, inp, passes, mask=None, budget_s: float = 15.0, max_heads: int = 32):
+    """Time the fp64 oracle (the same passes, whole heads) on the host cores."""
     import oracle
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
     oracle.build(force=False)
     threads = oracle.max_threads()
+    m = None if mask is None else mask.cpu().numpy()
+    kw = {} if m is None else {"block_mask": m, "mask_block": w.mask_block}
     done, t_total = 0, 0.0
-    while done < max_heads and t_total < budget_s:
+    while done < min(max_heads, w.B * w.H) and t_total < budget_s:
         b, h = divmod(done, w.H)
         t0 = time.perf_counter()
-        oracle.forward(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
-        oracle.backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+        oracle.forward(q[b, h], k[b, h], v[b, h], w.scale, w.causal, **kw)
+        if "bwd" in passes:
+            oracle.backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal, **kw)
         t_total += time.perf_counter() - t0
         done += 1
-    per_head = (flops(w, "fwd") + flops(w, "bwd")) / (w.B * w.H)
+    per_head = sum(flops(w, p, mask) for p in passes) / (w.B * w.H)
+    what = " + ".join({"fwd": "forward", "bwd": "backward"}[p] for p in passes)
     return {"value": round(per_head * done / t_total / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
-            "sample": f"{done} whole head(s) of the workload (forward + backward, all "
-                      f"{w.N} rows), {t_total:.1f} s, fp64, same FLOP convention"}
+            "sample": f"{done} whole head(s) of the workload ({what}, all {w.N} rows), "
+                      f"{t_total:.1f} s, fp64, same FLOP convention"}
+
+
+def roofline(w, which, ms, fl, traffic, kernel):
+    """The pass against MFMA peak, or HBM peak when its intensity is below the ridge."""
+    by = traffic_bytes(w, which)
+    tf = fl / (ms * 1e-3) / 1e12
+    gbs = by / (ms * 1e-3) / 1e9
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype != "f32" else 157.3
+    hbm = fl / by < RIDGE
+    r = {"bound": "hbm" if hbm else "mfma",
+         "achieved": round(gbs if hbm else tf, 2),
+         "peak": PEAK_HBM_GBS if hbm else peak_mfma,
+         "unit": "GB/s" if hbm else "TFLOP/s",
+         "frac": round(gbs / PEAK_HBM_GBS if hbm else tf / peak_mfma, 4),
+         "traffic": traffic, "kernel": kernel,
+         ("flops_per_launch" if which == "fwd" else "flops_per_call"): fl,
+         ("avg_launch_ms" if which == "fwd" else "avg_call_ms"): round(ms, 4),
+         ("algorithmic_bytes_per_launch" if which == "fwd" else
+          "algorithmic_bytes_per_call"): by,
+         "intensity_flop_per_byte": round(fl / by, 1),
+         "tflops": round(tf, 2), "gbs": round(gbs, 1)}
+    return r
 
 
 CEILING_SRC = os.path.join(ROOT, "bench_mfma_ceiling.hip")
@@ -139,6 +189,12 @@ def main():
                     help="HBM bytes per launch measured with rocprofv3 counters, if present")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="measure the sustained bf16 MFMA rate (bench_mfma_ceiling.hip) and exit")
+    ap.add_argument("--workload", default="long_d128_causal",
+                    help="named workload (exact_io_aware_45_amd.inputs.WORKLOADS)")
+    ap.add_argument("--causal", choices=("default", "on", "off"), default="default",
+                    help="override the workload's causal flag")
+    ap.add_argument("--passes", choices=("default", "fwd", "fwd+bwd"), default="default",
+                    help="forward only or forward + backward (default: per workload)")
     args = ap.parse_args()
 
     if args.mfma_ceiling:
@@ -149,10 +205,25 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
+    import dataclasses
+
     import torch
     from exact_io_aware_45_amd import _lib, inputs
 
-    w = inputs.WORKLOADS["long_d128_causal"]
+    if args.workload not in inputs.WORKLOADS:
+        print(json.dumps({"error": f"unknown workload {args.workload}",
+                          "workloads": sorted(inputs.WORKLOADS)}))
+        sys.exit(2)
+    w = inputs.WORKLOADS[args.workload]
+    if args.causal != "default":
+        w = dataclasses.replace(w, causal=args.causal == "on")
+    if args.passes == "default":
+        passes = ("fwd", "bwd") if (w.backward or w.name == "long_d128_causal") else ("fwd",)
+    else:
+        passes = tuple(args.passes.split("+"))
+    if w.dtype == "f32" and "bwd" in passes:
+        print(json.dumps({"error": "the fp32 path is forward only"}))
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     _lib.load()
@@ -168,16 +239,32 @@ def main():
     host = inputs.qkv(w.B, w.H, w.N, w.d, w.torch_dtype, args.seed, with_dout=True)
     inp = dict(zip(("q", "k", "v", "dout"), host))
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    mask = None
+    if w.sparse:
+        mask = inputs.block_mask(w.N, w.mask_block, w.band, w.density, args.seed)
+    maskd = None if mask is None else mask.to(dev)
     ws = torch.empty(max(1, _lib.backward_workspace_size(w.B, w.H, w.N, w.d)), dtype=torch.uint8,
                      device=dev)
+
+    def fwd():
+        if maskd is not None:
+            return _lib.forward_blocksparse(q, k, v, maskd, causal=w.causal)
+        return _lib.forward(q, k, v, causal=w.causal)
+
+    def bwd(o, lse):
+        if maskd is not None:
+            _lib.backward_blocksparse(q, k, v, o, do, lse, maskd, causal=w.causal, workspace=ws)
+        else:
+            _lib.backward(q, k, v, o, do, lse, causal=w.causal, workspace=ws)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        o, lse = _lib.forward(q, k, v, causal=w.causal)
+        o, lse = fwd()
         if ev is not None:
             ev[1].record()
-        _lib.backward(q, k, v, o, do, lse, causal=w.causal, workspace=ws)
+        if "bwd" in passes:
+            bwd(o, lse)
         if ev is not None:
             ev[2].record()
 
@@ -201,14 +288,21 @@ def main():
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms_per_step = total_ms / args.steps
 
-    ff, fb = flops(w, "fwd"), flops(w, "bwd")
+    ff = flops(w, "fwd", mask)
+    fb = flops(w, "bwd", mask) if "bwd" in passes else 0.0
     value = (ff + fb) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
-    bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
 
-    traffic = load_traffic(args.traffic_json)
+    # Counter-measured bytes exist only for the default workload's kernels.
+    traffic = load_traffic(args.traffic_json) if w.name == "long_d128_causal" else {}
 
+    mode = ("block-sparse " if w.sparse else "") + ("causal" if w.causal else "non-causal")
+    nw = 4 if w.sparse else 8
+    fwd_kernel = (f"fwd_f32_kernel<d={w.d}> (1 launch per fa_forward_f32)" if w.dtype == "f32"
+                  else f"fwd_bf16_kernel<d={w.d}, BC=64, {nw} waves, {mode}> "
+                       f"(1 launch per fa_forward{'_blocksparse' if w.sparse else ''})")
     props = torch.cuda.get_device_properties(dev)
+    peak = PEAK_BF16_TFLOPS if w.dtype != "f32" else 157.3
     line = {
         "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak, N=8192 d=128 causal",
         "value": round(value, 3),
@@ -220,34 +314,36 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic (i.i.d. N(0,1) Q, K, V, dO from a seeded generator)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "pass": "forward+backward", "seed": args.seed},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                   "causal": w.causal,
+                   "pass": "forward+backward" if "bwd" in passes else "forward",
+                   "seed": args.seed},
+        "frac_of_peak": round(value / peak, 4),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
-                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "flops": ff},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
-                "frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "flops": fb},
-        "roofline": {"bound": "mfma", "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic.get("fwd_bf16_kernel"),
-                     "kernel": "fwd_bf16_kernel<d=128, BC=64, 8 waves, causal> (1 launch per fa_forward)",
-                     "flops_per_launch": ff, "avg_launch_ms": round(fwd_ms, 4),
-                     "algorithmic_bytes_per_launch": traffic_bytes(w, "fwd")},
-        "roofline_bwd": {"bound": "mfma", "achieved": round(bwd_tf, 2),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic.get("fa_backward"),
-                         "kernel": "fa_backward call = bwd_delta + bwd_dkdv + bwd_dq launches",
-                         "flops_per_call": fb, "avg_call_ms": round(bwd_ms, 4),
-                         "algorithmic_bytes_per_call": traffic_bytes(w, "bwd")},
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "hip_runtime": _lib.runtime_version(), "libfa": _lib.version()},
-        "wall_s_timed_region": round(wall, 3),
+                "frac_of_peak": round(fwd_tf / peak, 4), "flops": ff},
+        "roofline": roofline(w, "fwd", fwd_ms, ff, traffic.get("fwd_bf16_kernel"), fwd_kernel),
     }
+    if w.sparse:
+        line["config"]["mask"] = {"tiles": int(mask.sum()), "of": int(mask.numel()),
+                                  "block": w.mask_block, "band": w.band,
+                                  "density": w.density}
+        line["dense_equivalent_fwd_tflops"] = round(
+            flops(dataclasses.replace(w, sparse=False), "fwd") / (fwd_ms * 1e-3) / 1e12, 2)
+    if "bwd" in passes:
+        bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
+        line["bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+                       "frac_of_peak": round(bwd_tf / peak, 4), "flops": fb}
+        line["roofline_bwd"] = roofline(
+            w, "bwd", bwd_ms, fb, traffic.get("fa_backward"),
+            f"fa_backward{'_blocksparse' if w.sparse else ''} call = bwd_delta + bwd_dkdv + "
+            "bwd_dq launches")
+    line["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                      "hip_runtime": _lib.runtime_version(), "libfa": _lib.version()}
+    line["wall_s_timed_region"] = round(wall, 3)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp)
+        line["cpu_baseline"] = cpu_baseline(w, inp, passes, mask)
     print(json.dumps(line), flush=True)
 
 

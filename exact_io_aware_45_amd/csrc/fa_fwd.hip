@@ -18,7 +18,8 @@
 //     the whole key loop;
 //   * K and V tiles of BC keys go HBM -> LDS with direct loads
 //     (global_load_lds_dwordx4, no register round trip), double buffered:
-//     the next tile's loads are in flight during the current tile's math.
+//     the next tile's loads are in flight during the current tile's math,
+//     and (dense d = 128) nothing waits for them before the tile's end;
 //     The tiles are unpadded with an XOR swizzle of the 16-byte chunks, which
 //     keeps both the K row reads and the V transpose reads conflict-free;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
@@ -77,7 +78,14 @@ void fwd_bf16_kernel(FwdArgs a) {
   constexpr int DC = D / 16;   // contraction steps of S^T = K Q^T
   constexpr int DB = D / 32;   // 32-row blocks of O^T
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (T::K_ELEMS + T::V_ELEMS)];
+  // One LDS array per tensor and stage.  The compiler tracks the direct loads
+  // into each array separately, so reading the current stage does not wait
+  // for the loads of the next one (with a single array it waits for them
+  // before the first read that might alias).
+  __shared__ __attribute__((aligned(16))) bf16 k_s0[T::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k_s1[T::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v_s0[T::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v_s1[T::V_ELEMS];
 
   const int N = a.N;
   const int nq = (N + kBR - 1) / kBR;
@@ -131,9 +139,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   // lane l of a wave's i-th load fills the 16 bytes at LDS position
   // p = (i * NW + wave) * 64 + l of the tile, i.e. row p / CH, slot p % CH,
   // which holds the row's chunk slot ^ swz(row).
-  auto load_tile = [&](int t, int stage) {
-    bf16* Ks = smem + stage * T::K_ELEMS;
-    bf16* Vs = smem + 2 * T::K_ELEMS + stage * T::V_ELEMS;
+  auto load_tile = [&](int t, bf16* Ks, bf16* Vs) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int base = (i * NW + wave) * 64;
@@ -156,9 +162,8 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   wait_global_loads();  // Q operands resident before the key loop
   int t = next_tile(0);
-  if (t < tend) load_tile(t, 0);
+  if (t < tend) load_tile(t, k_s0, v_s0);
   __syncthreads();
-  int stage = 0;
 
   // Lane-invariant parts of the swizzled LDS addresses.  K operand rows:
   // row 32kb + l32, chunk 2c + h.  V^T transpose reads: rows
@@ -172,12 +177,12 @@ void fwd_bf16_kernel(FwdArgs a) {
     return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
   };
 
-  while (t < tend) {
+  // One key tile: computes with (Ks, Vs) while the next visited tile lands
+  // in (Kn, Vn).
+  auto tile_step = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn) {
     const int tn = next_tile(t + 1);
-    if (tn < tend) load_tile(tn, stage ^ 1);  // lands during this tile's math
+    if (tn < tend) load_tile(tn, Kn, Vn);
 
-    const bf16* Ks = smem + stage * T::K_ELEMS;
-    const bf16* Vs = smem + 2 * T::K_ELEMS + stage * T::V_ELEMS;
     const int k0 = t * BC;
     // A causal tile entirely above this wave's rows contributes nothing.
     if (!kIsCausal || k0 <= q0 + 32 * wave + 31) {
@@ -186,14 +191,26 @@ void fwd_bf16_kernel(FwdArgs a) {
     // of query qrow.
     f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    // The NB accumulation chains alternate; for dense d = 128 every operand
+    // read is issued four matrix instructions ahead of its use.
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
         const bf16x8 ka = lds_read8(Ks + (32 * kb + l32) * D + 8 * ((2 * c + h) ^ sw_row));
         s[kb] = mfma32(ka, qf[c], s[kb]);
       }
+    if constexpr (D == 128 && !kIsSparse) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NB * DC - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     // Masking: causal tiles crossing this wave's diagonal, and the ragged tail.
@@ -254,8 +271,26 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 
     __syncthreads();  // also drains this wave's direct loads of tile tn
-    stage ^= 1;
     t = tn;
+  };
+  if constexpr (D == 128 && !kIsSparse) {
+    // Buffers named at compile time (two steps per trip), so that the reads
+    // of one stage are known not to alias the loads into the other.
+    while (t < tend) {
+      tile_step(k_s0, v_s0, k_s1, v_s1);
+      if (t >= tend) break;
+      tile_step(k_s1, v_s1, k_s0, v_s0);
+    }
+  } else {
+    // d = 64 keeps four waves per SIMD in 128 registers, and the tile-mask
+    // scan adds registers too: the two-step loop does not fit there, so the
+    // stage is chosen at run time.
+    int stage = 0;
+    while (t < tend) {
+      tile_step(stage ? k_s1 : k_s0, stage ? v_s1 : v_s0, stage ? k_s0 : k_s1,
+                stage ? v_s0 : v_s1);
+      stage ^= 1;
+    }
   }
 
   // Epilogue: O = acc / l (bf16), LSE = ln(sum) in natural units.

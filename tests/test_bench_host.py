@@ -1,0 +1,48 @@
+"""Host-side logic of bench.py (CPU only): FLOP conventions and pair counts."""
+import dataclasses
+
+import torch
+
+import bench
+from exact_io_aware_45_amd import inputs
+
+
+def brute_pairs(N, mb, mask, causal):
+    n = 0
+    for i in range(N):
+        for j in range(N):
+            if mask[i // mb, j // mb] and (not causal or j <= i):
+                n += 1
+    return n
+
+
+def test_visible_pairs_match_brute_force():
+    g = torch.Generator().manual_seed(3)
+    for N, causal in ((300, False), (300, True), (256, True), (77, False)):
+        w = dataclasses.replace(inputs.WORKLOADS["blocksparse_d64"], N=N, causal=causal,
+                                mask_block=64)
+        nb = -(-N // 64)
+        mask = (torch.rand(nb, nb, generator=g) < 0.6).to(torch.uint8)
+        assert bench.visible_pairs(w, mask) == brute_pairs(N, 64, mask, causal)
+
+
+def test_flop_conventions():
+    w = inputs.WORKLOADS["long_d128_causal"]
+    assert bench.flops(w, "fwd") == 4 * 32 * 8192 ** 2 * 128 / 2
+    assert bench.flops(w, "bwd") == 10 * 32 * 8192 ** 2 * 128 / 2
+    s = inputs.WORKLOADS["blocksparse_d64"]
+    m = inputs.block_mask(s.N, 128, 1, 0.125, 0)
+    assert bench.flops(s, "fwd", m) == 4 * 16 * 64 * 2048 * 128 * 128
+    full = torch.ones(128, 128, dtype=torch.uint8)
+    dense = dataclasses.replace(s, sparse=False)
+    assert bench.flops(s, "fwd", full) == bench.flops(dense, "fwd")
+
+
+def test_roofline_picks_the_bound_by_intensity():
+    causal = inputs.WORKLOADS["batched_d64_causal"]
+    r = bench.roofline(causal, "fwd", 0.01, bench.flops(causal, "fwd"), None, "k")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    long = inputs.WORKLOADS["long_d128_causal"]
+    r = bench.roofline(long, "fwd", 0.5, bench.flops(long, "fwd"), None, "k")
+    assert r["bound"] == "mfma" and abs(r["frac"] - bench.flops(long, "fwd") / 0.5e-3 / 1e12
+                                        / bench.PEAK_BF16_TFLOPS) < 1e-4
