@@ -33,10 +33,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense; published 2.5 PF)
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 fp8 FLOP/clk/CU (dense; published 5.0 PF)
+PEAK_F32_TFLOPS = 157.3
+
+
+def mfma_peak(w) -> float:
+    return {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(w.dtype, PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 
-RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 
 
 def visible_pairs(w, mask) -> float:
@@ -62,11 +67,12 @@ def flops(w, which: str, mask=None) -> float:
 
 def traffic_bytes(w, which: str) -> float:
     """Algorithmic HBM bytes of one call: read the inputs once, write the outputs once."""
-    es = 4.0 if w.dtype == "f32" else 2.0
+    es = {"f32": 4.0, "fp8": 1.0}.get(w.dtype, 2.0)
     t = w.B * w.H * w.N * w.d * es   # one input-dtype tensor
+    to = w.B * w.H * w.N * w.d * (4.0 if w.dtype == "f32" else 2.0)  # O (bf16 unless fp32)
     rows = w.B * w.H * w.N * 4.0     # one fp32 [B,H,N] vector
     if which == "fwd":
-        return 3 * t + t + rows                 # Q K V in, O + LSE out
+        return 3 * t + to + rows                # Q K V in, O + LSE out
     return 5 * t + rows + 3 * 2 * t + 2 * rows  # Q K V O dO + LSE in; fp32 dQ dK dV out; D out/in
 
 
@@ -126,8 +132,8 @@ def roofline(w, which, ms, fl, traffic, kernel):
     by = traffic_bytes(w, which)
     tf = fl / (ms * 1e-3) / 1e12
     gbs = by / (ms * 1e-3) / 1e9
-    peak_mfma = PEAK_BF16_TFLOPS if w.dtype != "f32" else 157.3
-    hbm = fl / by < RIDGE
+    peak_mfma = mfma_peak(w)
+    hbm = fl / by < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
     r = {"bound": "hbm" if hbm else "mfma",
          "achieved": round(gbs if hbm else tf, 2),
          "peak": PEAK_HBM_GBS if hbm else peak_mfma,
@@ -195,6 +201,8 @@ def main():
                     help="override the workload's causal flag")
     ap.add_argument("--passes", choices=("default", "fwd", "fwd+bwd"), default="default",
                     help="forward only or forward + backward (default: per workload)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="fp8 (OCP e4m3) inputs through fa_forward_fp8, forward only")
     args = ap.parse_args()
 
     if args.mfma_ceiling:
@@ -221,6 +229,12 @@ def main():
         passes = ("fwd", "bwd") if (w.backward or w.name == "long_d128_causal") else ("fwd",)
     else:
         passes = tuple(args.passes.split("+"))
+    if args.fp8:
+        if w.dtype != "bf16" or w.sparse or args.passes == "fwd+bwd":
+            print(json.dumps({"error": "fp8 runs the dense bf16 workloads, forward only"}))
+            sys.exit(2)
+        w = dataclasses.replace(w, dtype="fp8")
+        passes = ("fwd",)
     if w.dtype == "f32" and "bwd" in passes:
         print(json.dumps({"error": "the fp32 path is forward only"}))
         sys.exit(2)
@@ -236,9 +250,18 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    host = inputs.qkv(w.B, w.H, w.N, w.d, w.torch_dtype, args.seed, with_dout=True)
-    inp = dict(zip(("q", "k", "v", "dout"), host))
-    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    if w.dtype == "fp8":
+        f8 = inputs.qkv_fp8(w.B, w.H, w.N, w.d, args.seed)
+        descales = [x[1] for x in f8]
+        q, k, v = (x[0].to(dev) for x in f8)
+        do = None
+        # the oracle baseline runs on the dequantized values
+        inp = {n: x[0].to(torch.float32) * x[1] for n, x in zip(("q", "k", "v"), f8)}
+        inp["dout"] = None
+    else:
+        host = inputs.qkv(w.B, w.H, w.N, w.d, w.torch_dtype, args.seed, with_dout=True)
+        inp = dict(zip(("q", "k", "v", "dout"), host))
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
     mask = None
     if w.sparse:
         mask = inputs.block_mask(w.N, w.mask_block, w.band, w.density, args.seed)
@@ -247,6 +270,8 @@ def main():
                      device=dev)
 
     def fwd():
+        if w.dtype == "fp8":
+            return _lib.forward_fp8(q, k, v, *descales, causal=w.causal)
         if maskd is not None:
             return _lib.forward_blocksparse(q, k, v, maskd, causal=w.causal)
         return _lib.forward(q, k, v, causal=w.causal)
@@ -294,15 +319,21 @@ def main():
     fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
 
     # Counter-measured bytes exist only for the default workload's kernels.
-    traffic = load_traffic(args.traffic_json) if w.name == "long_d128_causal" else {}
+    traffic = (load_traffic(args.traffic_json)
+               if w.name == "long_d128_causal" and w.dtype == "bf16" else {})
 
     mode = ("block-sparse " if w.sparse else "") + ("causal" if w.causal else "non-causal")
     nw = 4 if w.sparse else 8
-    fwd_kernel = (f"fwd_f32_kernel<d={w.d}> (1 launch per fa_forward_f32)" if w.dtype == "f32"
-                  else f"fwd_bf16_kernel<d={w.d}, BC=64, {nw} waves, {mode}> "
-                       f"(1 launch per fa_forward{'_blocksparse' if w.sparse else ''})")
+    if w.dtype == "f32":
+        fwd_kernel = f"fwd_f32_kernel<d={w.d}> (1 launch per fa_forward_f32)"
+    elif w.dtype == "fp8":
+        fwd_kernel = (f"fwd_fp8_kernel<d={w.d}, BC=64, {8 if w.d == 128 else 4} waves, {mode}> "
+                      "(1 launch per fa_forward_fp8)")
+    else:
+        fwd_kernel = (f"fwd_bf16_kernel<d={w.d}, BC=64, {nw} waves, {mode}> "
+                      f"(1 launch per fa_forward{'_blocksparse' if w.sparse else ''})")
     props = torch.cuda.get_device_properties(dev)
-    peak = PEAK_BF16_TFLOPS if w.dtype != "f32" else 157.3
+    peak = mfma_peak(w)
     line = {
         "metric": "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak, N=8192 d=128 causal",
         "value": round(value, 3),
@@ -314,7 +345,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "dtype": {"f32": "f32", "fp8": "fp8-e4m3"}.get(w.dtype, "bf16"),
         "data": "synthetic (i.i.d. N(0,1) Q, K, V, dO from a seeded generator)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal,

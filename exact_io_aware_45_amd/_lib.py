@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(_HERE, "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 SYMBOLS = ("fa_forward", "fa_forward_f32", "fa_backward_workspace_size", "fa_backward",
            "fa_forward_blocksparse", "fa_backward_blocksparse", "fa_forward_gqa",
-           "fa_backward_gqa", "fa_error_string", "fa_version", "fa_runtime_version")
+           "fa_backward_gqa", "fa_forward_fp8", "fa_error_string", "fa_version",
+           "fa_runtime_version")
 
 _lib = None
 
@@ -51,11 +52,12 @@ def load():
     lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i,
                                             i, f, i, vp, i, vp]
     lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, f, f, f, i, vp]
     lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f,
                                     i, vp]
     for name in ("fa_forward", "fa_forward_f32", "fa_forward_blocksparse", "fa_backward",
                  "fa_backward_blocksparse", "fa_forward_gqa", "fa_backward_gqa",
-                 "fa_version", "fa_runtime_version"):
+                 "fa_forward_fp8", "fa_version", "fa_runtime_version"):
         getattr(lib, name).restype = i
     lib.fa_error_string.argtypes = [i]
     lib.fa_error_string.restype = ctypes.c_char_p
@@ -171,6 +173,20 @@ def forward_gqa(q, k, v, causal: bool = False, scale: float | None = None):
     _check(lib.fa_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
                               _scale(scale, d), int(bool(causal)), _stream(q.device)),
            "fa_forward_gqa")
+    return o, lse
+
+
+def forward_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
+                causal: bool = False, scale: float | None = None):
+    """fa_forward_fp8: q, k, v torch.float8_e4m3fn [B,H,N,d] codes; returns (o bf16, lse)."""
+    lib = load()
+    B, H, _, N, d = _shape(q, k, v, torch.float8_e4m3fn)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lib.fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                              _scale(scale, d), float(q_descale), float(k_descale),
+                              float(v_descale), int(bool(causal)), _stream(q.device)),
+           "fa_forward_fp8")
     return o, lse
 
 

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -47,11 +47,14 @@ int forward_common(const void* q, const void* k, const void* v, void* o, float* 
   if ((st = check_groups(H, Hkv)) != FA_OK) return st;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return FA_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, mask, mask_block, Hkv};
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, mask, mask_block, Hkv,
+                1.f, 1.f, 1.f};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // do not report an earlier, unrelated error
   return hip_status(f32 ? fa::launch_fwd_f32(a, s) : fa::launch_fwd_bf16(a, s));
 }
+
+bool positive_finite(float x) { return isfinite(x) && x > 0.f; }
 
 size_t workspace_size(int B, int H, int N, int d) {
   bool empty = false;
@@ -121,6 +124,23 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
   if (Hkv < 0) return FA_ERR_INVALID_ARG;
   return forward_common(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, nullptr, 0, false,
                         stream);
+}
+
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+                   int causal, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, scale, &empty);
+  if (st != FA_OK) return st;
+  if (!positive_finite(q_descale) || !positive_finite(k_descale) || !positive_finite(v_descale))
+    return FA_ERR_INVALID_ARG;
+  if (empty) return FA_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal ? 1 : 0, nullptr, 0, H,
+                q_descale, k_descale, v_descale};
+  (void)hipGetLastError();
+  return hip_status(fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {

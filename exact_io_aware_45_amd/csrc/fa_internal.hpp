@@ -21,6 +21,8 @@ struct FwdArgs {
   const uint8_t* mask;  // tile mask [nmb][nmb] or nullptr
   int mask_block;       // tile edge of the mask (keys and queries)
   int Hkv;
+  // fp8 inputs only: the real value of a stored element is element * descale.
+  float q_descale, k_descale, v_descale;
 };
 
 struct BwdArgs {
@@ -44,6 +46,7 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -9,6 +9,8 @@ synthetic):
     one CPU ``torch.Generator`` seeded with ``seed``, in the order Q, K, V, dO,
     each shaped [B, H, N, d], then rounded to the working dtype (bf16 by
     round-to-nearest-even, or kept float32).
+  * fp8 inputs: the same fp32 draws stored as OCP e4m3 codes with one
+    per-tensor descale amax / 448 (``qkv_fp8``).
   * The block-sparse tile mask is the symmetric diagonal band |qb - kb| <= band
     plus off-band tiles drawn uniformly without replacement (a CPU generator
     seeded ``seed + 1000``) until ``round(density * nb * nb)`` tiles are set.
@@ -72,6 +74,25 @@ def qkv(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0,
         t = torch.randn(shape, generator=g, dtype=torch.float32)
         out.append(t.to(dtype).contiguous().to(device))
     return tuple(out)
+
+
+FP8_MAX = 448.0  # largest finite OCP e4m3 value
+
+
+def qkv_fp8(B: int, H: int, N: int, d: int, seed: int = 0, device="cpu"):
+    """Q, K, V drawn exactly as ``qkv`` draws them (fp32), then stored as OCP
+    e4m3 codes (torch.float8_e4m3fn) with one fp32 descale per tensor,
+    descale = amax / 448, so that code * descale approximates the draw.
+
+    Returns [(q_codes, q_descale), (k_codes, k_descale), (v_codes, v_descale)].
+    """
+    out = []
+    for t in qkv(B, H, N, d, torch.float32, seed):
+        amax = float(t.abs().max())
+        descale = float(torch.tensor(amax / FP8_MAX if amax > 0 else 1.0, dtype=torch.float32))
+        codes = (t / descale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+        out.append((codes.contiguous().to(device), descale))
+    return out
 
 
 def block_mask(N: int, mask_block: int = 128, band: int = 1, density: float = 0.125,

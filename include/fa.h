@@ -157,6 +157,24 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                     size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
                     int causal, void* stream);
 
+/*
+ * Forward pass with fp8 inputs: q, k, v hold OCP e4m3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; largest finite value 448) in
+ * the fa_forward layout, one byte per element, and the real value of an
+ * element is code * descale (one fp32 descale per tensor, finite and > 0,
+ * else FA_ERR_INVALID_ARG).  Both products run on the 8-bit matrix cores
+ * with fp32 accumulation; the attention weights are rounded to e4m3 for the
+ * second product.  Lower-precision matrix inputs are the direction the
+ * "FlashAttention." plate's "Never write the scores" section gives for the
+ * H100 generation of the method.
+ *   o    out: bf16 [B][H][N][d]
+ *   lse  out: fp32 [B][H][N], of scale * (q_descale q)(k_descale k)^T
+ * d in {64, 128}; causal as fa_forward.
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+                   int causal, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_error_string(int status);
 

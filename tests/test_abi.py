@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("fa_forward", "fa_backward", "fa_forward_blocksparse", "fa_backward_blocksparse",
-              "fa_forward_gqa", "fa_backward_gqa"):
+              "fa_forward_gqa", "fa_backward_gqa", "fa_forward_fp8"):
         assert n in names
     assert set(names) == set(_lib.SYMBOLS)
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_error_strings():
     lib = _lib.load()
-    assert _lib.version() == 200
+    assert _lib.version() == 300
     for st in range(4):
         s = _lib.error_string(st)
         assert isinstance(s, str) and s
@@ -166,3 +166,20 @@ def test_gqa_argument_errors():
     assert bwd_g(Hkv=0) == INV
     assert bwd_g(dk=None) == INV
     assert bwd_g(ws_bytes=ws - 4) == INV
+
+
+def test_fp8_argument_errors():
+    lib = _lib.load()
+    INV = _lib.FA_ERR_INVALID_ARG
+
+    def f8(qs=0.01, ks=0.01, vs=0.01, q=FAKE, d=128, N=64):
+        return lib.fa_forward_fp8(q, FAKE, FAKE, FAKE, FAKE, 1, 2, N, d, 0.088, qs, ks, vs, 1, None)
+
+    assert f8(qs=0.0) == INV
+    assert f8(ks=-1.0) == INV
+    assert f8(vs=float("nan")) == INV
+    assert f8(vs=float("inf")) == INV
+    assert f8(q=None) == INV
+    assert f8(q=MIS) == INV
+    assert f8(d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert f8(q=None, N=0) == _lib.FA_OK

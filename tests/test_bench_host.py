@@ -46,3 +46,11 @@ def test_roofline_picks_the_bound_by_intensity():
     r = bench.roofline(long, "fwd", 0.5, bench.flops(long, "fwd"), None, "k")
     assert r["bound"] == "mfma" and abs(r["frac"] - bench.flops(long, "fwd") / 0.5e-3 / 1e12
                                         / bench.PEAK_BF16_TFLOPS) < 1e-4
+
+
+def test_fp8_traffic_and_peak():
+    import dataclasses as dc
+    w = dc.replace(inputs.WORKLOADS["long_d128_causal"], dtype="fp8")
+    t = 32 * 8192 * 128
+    assert bench.traffic_bytes(w, "fwd") == 3 * t + 2 * t + 32 * 8192 * 4
+    assert bench.mfma_peak(w) == 2 * bench.PEAK_BF16_TFLOPS

@@ -365,3 +365,83 @@ def test_gqa_with_hkv_equal_h_is_plain_attention():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ fp8
+# The fp8 forward is compared with the oracle on the dequantized inputs
+# (code * descale, exact in fp64).  Its one rounding beyond fp32 level is the
+# attention weights' conversion to e4m3 for the second product: weights are
+# stored as w' = 2^8 exp(s - m), rounded with relative error <= 2^-4 in the
+# normal range and absolute error <= 2^-10 below it, and the row sum uses the
+# unrounded weights.  So, per output element,
+#   |dO_c| <= sum_j (2^-4 w_j + 2^-10 / L') |v_jc| + fp32 accumulation + bf16 output,
+# with w_j = exp(s_j - LSE) the oracle's weights and L' = 2^8 sum_j exp(s_j - m) >= 2^8.
+# (The bf16 tolerance of the other tests does not apply: e4m3 keeps 3 mantissa
+# bits, so a row with few visible keys can legitimately miss by more.)
+def fp8_dequant(codes, descale, pairs):
+    return np.stack([codes[b, h].to(torch.float64).numpy() * descale for b, h in pairs])
+
+
+def fp8_bound(qd, kd, vd, lse, scale, causal):
+    """Per-element error bound [n, N, d] for the fp8 forward (fp64, row chunks)."""
+    n, N, d = qd.shape
+    out = np.zeros_like(qd)
+    for i in range(n):
+        for r0 in range(0, N, 512):
+            s = scale * qd[i, r0:r0 + 512] @ kd[i].T
+            rows = np.arange(r0, min(r0 + 512, N))
+            if causal:
+                s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
+            w = np.exp(s - lse[i, r0:r0 + 512, None])
+            visible = np.isfinite(s)
+            absv = np.abs(vd[i])
+            rel = 2.0 ** -4 + N * 2.0 ** -24 + 1e-5
+            out[i, r0:r0 + 512] = rel * (w @ absv) + 2.0 ** -18 * (visible @ absv)
+    return out
+
+
+def fp8_parity(B, H, N, d, causal, seed, pairs=None):
+    (q8, qs), (k8, ks), (v8, vs) = inputs.qkv_fp8(B, H, N, d, seed=seed)
+    o, lse = _lib.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), qs, ks, vs, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    pairs = pairs or all_pairs(q8)
+    qd, kd, vd = (fp8_dequant(c, s, pairs) for c, s in ((q8, qs), (k8, ks), (v8, vs)))
+    scale = d ** -0.5
+    ro, rl = oracle.forward(qd, kd, vd, scale, causal)
+    go = np.stack([to64(o[b, h]) for b, h in pairs])
+    gl = np.stack([to64(lse[b, h]) for b, h in pairs])
+    err = np.abs(go - ro)
+    bound = fp8_bound(qd, kd, vd, rl, scale, causal) + 2.0 ** -9 * np.abs(ro) + 1e-6
+    log(f"  fp8 O: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
+        f"max err/bound={float((err / bound).max()):.3f}")
+    assert bool((err <= bound).all()), "fp8 O outside its derived error bound"
+    # The bound lines every rounding up against the output; independent
+    # roundings leave the typical element far inside it.  A systematic error
+    # (a wrong scale, a biased rounding) would not.
+    assert err.mean() <= 0.25 * bound.mean(), (err.mean(), bound.mean())
+    lerr = np.abs(gl - rl)
+    log(f"  fp8 LSE: max_abs={lerr.max():.3e}")
+    assert lerr.max() <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 200, 333])
+def test_fp8_forward_small(N, d, causal):
+    need_gpu()
+    log(f"fp8 forward B2 H2 N{N} d{d} causal={causal}")
+    fp8_parity(2, 2, N, d, causal, seed=N + 3 * d)
+
+
+def test_fp8_forward_long_workload():
+    """The long causal shape (B1 H32 N8192 d128) in fp8, two sampled heads."""
+    need_gpu()
+    log("fp8 forward B1 H32 N8192 d128 causal")
+    fp8_parity(1, 32, 8192, 128, True, seed=0, pairs=sample_pairs(1, 32, 2, 0))
+
+
+def test_fp8_forward_batched_workload():
+    need_gpu()
+    log("fp8 forward B8 H16 N1024 d64 non-causal")
+    fp8_parity(8, 16, 1024, 64, False, seed=1, pairs=sample_pairs(8, 16, 3, 1))

@@ -34,3 +34,17 @@ def test_workload_shapes():
     assert w["bwd_d128_causal"].backward and w["long_d128_causal"].causal
     assert w["blocksparse_d64"].sparse and w["blocksparse_d64"].N == 16384
     assert w["single_head_f32"].dtype == "f32"
+
+
+def test_fp8_inputs_quantize_the_same_draws():
+    ref = inputs.qkv(1, 2, 100, 64, torch.float32, seed=3)
+    for (codes, descale), x in zip(inputs.qkv_fp8(1, 2, 100, 64, seed=3), ref):
+        assert codes.dtype == torch.float8_e4m3fn and codes.shape == x.shape
+        real = codes.to(torch.float64) * descale
+        assert float(codes.to(torch.float32).abs().max()) <= inputs.FP8_MAX
+        # e4m3 rounding: relative error <= 2^-4 in the normal range, absolute
+        # <= 2^-10 * descale below it
+        err = (real - x.to(torch.float64)).abs()
+        bound = 2.0 ** -4 * x.to(torch.float64).abs() + 2.0 ** -10 * descale + 1e-12
+        assert bool((err <= bound).all())
+        assert abs(float(x.abs().max()) / inputs.FP8_MAX - descale) <= 1e-6 * descale
