@@ -231,16 +231,23 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = half_pair_max(mx);
-    const float m_new = fmaxf(m_ref, mx * sl2);
-    if (m_new > m_ref + kRescaleThreshold) {
-      const float alpha = fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
+    // The two halves of the wave hold different keys of one query row, so the
+    // reference must be their common maximum; but it only has to move when a
+    // maximum exceeds it by more than the threshold.  The exchange between
+    // the halves is done only when some lane of the wave sees that (rare once
+    // the first tiles have set the reference).
+    if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_ref + kRescaleThreshold) != 0) {
+      mx = half_pair_max(mx);
+      const float m_new = fmaxf(m_ref, mx * sl2);
+      if (m_new > m_ref + kRescaleThreshold) {
+        const float alpha = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      }
     }
     const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll

@@ -37,7 +37,6 @@
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
-#include <type_traits>
 
 namespace fa {
 
@@ -215,16 +214,20 @@ void fwd_fp8_kernel(FwdArgs a) {
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_pair_max(mx);
-      const float m_new = fmaxf(m_ref, mx * sl2);
-      if (m_new > m_ref) {
-        const float alpha = fast_exp2(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
+      // The halves' maxima are exchanged only when some lane's maximum
+      // exceeds the reference (the two halves hold keys of one query row).
+      if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_ref) != 0) {
+        mx = half_pair_max(mx);
+        const float m_new = fmaxf(m_ref, mx * sl2);
+        if (m_new > m_ref) {
+          const float alpha = fast_exp2(m_ref - m_new);
+          m_ref = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+          for (int b = 0; b < DB; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+            for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        }
       }
       const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
