@@ -19,13 +19,15 @@
 //
 // Three launches on the caller's stream, deterministic (no atomics):
 //   1. bwd_delta: D_i = dO_i . O_i (fp32), into the caller's workspace;
-//   2. bwd_dkdv:  one workgroup per 256 keys; each wave keeps 32 keys' K and V
+//   2. bwd_dkdv:  one workgroup per 128 keys (d=128) or 256 keys (d=64); each
+//      wave keeps 32 keys' K and V
 //      in registers and loops over 64-query tiles of Q and dO staged in LDS:
 //      S = Q K^T and dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE),
 //      dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read from
 //      the row-major LDS tiles by transpose reads;
 //   3. bwd_dq:    one workgroup per 128 queries; each wave keeps 32 queries'
-//      Q and dO in registers and loops over 64-key tiles of K and V in LDS:
+//      Q and dO in registers and loops over 64-key tiles of K and V, staged in
+//      LDS by direct loads:
 //      S^T = K Q^T, dP^T = V dO^T (lane = query column), dS^T, and
 //      dQ^T += K^T dS^T with K^T read by transpose reads.
 #include "fa_common.hpp"
@@ -173,8 +175,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // HBM -> LDS direct loads of one 64-query tile of Q and dO (swizzled, as
-  // tile_off lays it out) plus its LSE and D rows.
+  // HBM -> LDS direct loads of one 64-query tile of Q and dO (16-byte chunk q
+  // of row r stored at chunk q ^ tile_swz(r)) plus its LSE and D rows.
   auto load_tile = [&](Pos p, int st) {
     const size_t ho = (size_t)p.g * N * D;
 #pragma unroll
@@ -337,7 +339,11 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int DB = D / 32;
   constexpr int NB = T::BK / 32;
 
-  __shared__ __attribute__((aligned(16))) bf16 tiles[2][2][T::T_ELEMS];  // [stage][K|V]
+  // One LDS array per tensor and stage (see tile_step).
+  __shared__ __attribute__((aligned(16))) bf16 k_s0[T::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k_s1[T::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v_s0[T::T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v_s1[T::T_ELEMS];
 
   const int N = a.N;
   const int nqt = (N + T::BQ - 1) / T::BQ;
@@ -396,23 +402,19 @@ void bwd_dq_kernel(BwdArgs a) {
     return t;
   };
 
-  u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  auto load_tile = [&](int t) {
+  // HBM -> LDS direct loads of one key tile of K and V (chunk q of row r at
+  // chunk q ^ tile_swz(r)): lane l of a wave's i-th load fills LDS position
+  // p = (i * 4 + wave) * 64 + l, i.e. row p / CH, slot p % CH.
+  auto load_tile = [&](int t, bf16* Kd, bf16* Vd) {
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int k = min(t * T::BK + idx / T::CH, N - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(K + (size_t)k * D + 8 * (idx % T::CH));
-      vreg[i] = *reinterpret_cast<const u32x4*>(V + (size_t)k * D + 8 * (idx % T::CH));
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int off = tile_off<D>(idx / T::CH, idx % T::CH);
-      lds_write16(&tiles[stage][0][off], kreg[i]);
-      lds_write16(&tiles[stage][1][off], vreg[i]);
+      const int base = (i * 4 + wave) * 64;
+      const int p = base + lane;
+      const int row = p / T::CH;
+      const int q = (p % T::CH) ^ tile_swz<D>(row);
+      const size_t src = (size_t)min(t * T::BK + row, N - 1) * D + 8 * q;
+      lds_load16(K + src, Kd + 8 * base);
+      lds_load16(V + src, Vd + 8 * base);
     }
   };
 
@@ -427,17 +429,13 @@ void bwd_dq_kernel(BwdArgs a) {
 
   wait_global_loads();  // Q, dO operands resident before the key loop
   int t = next_tile(0);
-  if (t < tend) {
-    load_tile(t);
-    store_tile(0);
-  }
+  if (t < tend) load_tile(t, k_s0, v_s0);
   __syncthreads();
-  int stage = 0;
-  while (t < tend) {
+  // One key tile: computes with (Ks, Vs) while the next visited tile lands in
+  // (Kn, Vn).
+  auto tile_step = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn) {
     const int tn = next_tile(t + 1);
-    if (tn < tend) load_tile(tn);
-    const bf16* Ks = tiles[stage][0];
-    const bf16* Vs = tiles[stage][1];
+    if (tn < tend) load_tile(tn, Kn, Vn);
     const int k0 = t * T::BK;
     const bool need_mask = (CAUSAL && k0 + T::BK - 1 > q0 + 32 * wave) || (k0 + T::BK > N);
 #pragma unroll
@@ -479,10 +477,13 @@ void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    if (tn < tend) store_tile(stage ^ 1);
-    __syncthreads();
-    stage ^= 1;
+    __syncthreads();  // also drains this wave's direct loads of tile tn
     t = tn;
+  };
+  int stage = 0;
+  while (t < tend) {
+    tile_step(stage ? k_s1 : k_s0, stage ? v_s1 : v_s0, stage ? k_s0 : k_s1, stage ? v_s0 : v_s1);
+    stage ^= 1;
   }
 
   if (qrow < N) {

@@ -45,10 +45,6 @@ __device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
   return *(const FA_LDS bf16x8*)(p);
 }
 
-__device__ __forceinline__ void lds_write16(bf16* p, u32x4 v) {
-  *(FA_LDS u32x4*)(p) = v;
-}
-
 // Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
 // l's 16 bytes from `src` land at lds_base + 16 * l.  lds_base must be the
 // same for every lane of the wave.  Completion is tracked by the vector
@@ -134,12 +130,6 @@ __device__ __forceinline__ int tile_swz(int r) {
   static_assert(D == 64 || D == 128, "head dim");
   if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
   else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
-// Element offset of (row r, 16-byte chunk q) in a swizzled D-wide tile.
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int q) {
-  return r * D + 8 * (q ^ tile_swz<D>(r));
 }
 
 // Workgroup index -> work item, so that consecutive items stay on one XCD
