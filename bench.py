@@ -19,6 +19,9 @@ on.  Prints ONE JSON line:
 
 --workload runs one of the other named workloads (exact_io_aware_45_amd.inputs)
 with the same line format; forward-only workloads time fa_forward alone.
+--fp8 runs a dense workload's forward through fa_forward_fp8 (e4m3 inputs),
+priced against the fp8 peak.  --cold writes a 512 MiB buffer before every step
+(untimed), so that the inputs come from HBM rather than the last-level cache.
 """
 from __future__ import annotations
 
@@ -34,14 +37,13 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense; published 2.5 PF)
 PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 fp8 FLOP/clk/CU (dense; published 5.0 PF)
-PEAK_F32_TFLOPS = 157.3
-
-
-def mfma_peak(w) -> float:
-    return {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(w.dtype, PEAK_BF16_TFLOPS)
+PEAK_F32_TFLOPS = 157.3     # fp32 vector
 PEAK_HBM_GBS = 8000.0
 
 
+def mfma_peak(w) -> float:
+    """Dense peak of the arithmetic the workload's forward runs in (TFLOP/s)."""
+    return {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(w.dtype, PEAK_BF16_TFLOPS)
 
 
 def visible_pairs(w, mask) -> float:
@@ -201,6 +203,9 @@ def main():
                     help="override the workload's causal flag")
     ap.add_argument("--passes", choices=("default", "fwd", "fwd+bwd"), default="default",
                     help="forward only or forward + backward (default: per workload)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB buffer before every step (outside the timed passes) so "
+                         "the inputs are not served from the 256 MB last-level cache")
     ap.add_argument("--fp8", action="store_true",
                     help="fp8 (OCP e4m3) inputs through fa_forward_fp8, forward only")
     args = ap.parse_args()
@@ -302,8 +307,11 @@ def main():
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    flush = (torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None)
     start.record()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 255)
         step(evs[i])
     end.record()
     torch.cuda.synchronize()
@@ -311,7 +319,8 @@ def main():
     total_ms = start.elapsed_time(end)
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_per_step = total_ms / args.steps
+    # cold runs: the step is the passes alone (the flush between them is not timed)
+    ms_per_step = (fwd_ms + bwd_ms) if args.cold else total_ms / args.steps
 
     ff = flops(w, "fwd", mask)
     fb = flops(w, "bwd", mask) if "bwd" in passes else 0.0
@@ -350,6 +359,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal,
                    "pass": "forward+backward" if "bwd" in passes else "forward",
+                   "cache": "cold" if args.cold else "warm",
                    "seed": args.seed},
         "frac_of_peak": round(value / peak, 4),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
