@@ -45,6 +45,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr int kAcc = 4;  // independent partial maxima and sums per lane
 
 enum Mode { kDense = 0, kCausal = 1, kSparse = 2, kSparseCausal = 3 };
 
@@ -157,7 +158,12 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m_ref = -INFINITY;  // reference maximum (log2 units) of the exponentials
-  float l_run = 0.f;        // running sum over this lane's keys
+  // Running sum over this lane's keys, as kAcc independent partial sums
+  // (one chain of 32 dependent adds per tile would stall every tile; the
+  // row maximum is likewise taken over kAcc partial maxima).
+  float l_part[kAcc];
+#pragma unroll
+  for (int i = 0; i < kAcc; ++i) l_part[i] = 0.f;
   const float sl2 = a.scale * kLog2e;
 
   wait_global_loads();  // Q operands resident before the key loop
@@ -226,11 +232,18 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 
     // Online softmax (base 2).
-    float mx = -INFINITY;
+    float mpart[kAcc];
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) mpart[i] = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mpart[r % kAcc] = fmaxf(mpart[r % kAcc], s[kb][r]);
+#pragma unroll
+    for (int st = kAcc / 2; st > 0; st /= 2)
+#pragma unroll
+      for (int i = 0; i < st; ++i) mpart[i] = fmaxf(mpart[i], mpart[i + st]);
+    float mx = mpart[0];
     // The two halves of the wave hold different keys of one query row, so the
     // reference must be their common maximum; but it only has to move when a
     // maximum exceeds it by more than the threshold.  The exchange between
@@ -242,7 +255,8 @@ void fwd_bf16_kernel(FwdArgs a) {
       if (m_new > m_ref + kRescaleThreshold) {
         const float alpha = fast_exp2(m_ref - m_new);
         m_ref = m_new;
-        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < kAcc; ++i) l_part[i] *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -256,7 +270,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(s[kb][r], sl2, -mu));
         s[kb][r] = p;
-        l_run += p;
+        l_part[r % kAcc] += p;
       }
 
     // O^T += V^T P^T.
@@ -301,7 +315,11 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // Epilogue: O = acc / l (bf16), LSE = ln(sum) in natural units.
-  const float l_tot = half_pair_sum(l_run);
+#pragma unroll
+  for (int st = kAcc / 2; st > 0; st /= 2)
+#pragma unroll
+    for (int i = 0; i < st; ++i) l_part[i] += l_part[i + st];
+  const float l_tot = half_pair_sum(l_part[0]);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qrow < N) {
     if (h == 0)

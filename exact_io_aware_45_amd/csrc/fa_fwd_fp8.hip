@@ -50,6 +50,7 @@ typedef unsigned char u8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kPShift = 8.0f;  // log2 of the factor the stored weights carry
+constexpr int kAcc = 4;          // independent partial maxima and sums per lane
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   // formats 0/0 = e4m3 for A and B; scale exponents 127 = 2^0
@@ -167,7 +168,11 @@ void fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float m_ref = -INFINITY;  // running maximum (log2 units) of the scores
-  float l_run = 0.f;        // running sum of this lane's shifted weights
+  // Running sum of this lane's shifted weights, in kAcc independent parts
+  // (one chain of dependent adds would stall every tile).
+  float l_part[kAcc];
+#pragma unroll
+  for (int i = 0; i < kAcc; ++i) l_part[i] = 0.f;
   const float sl2 = a.scale * a.q_descale * a.k_descale * kLog2e;
 
   // Lane-invariant address parts.  K operand rows 32kb + l32, chunks
@@ -209,11 +214,14 @@ void fwd_fp8_kernel(FwdArgs a) {
           }
       }
       // Online softmax (base 2), maximum updated whenever it grows.
-      float mx = -INFINITY;
+      float mpart[kAcc];
+#pragma unroll
+      for (int i = 0; i < kAcc; ++i) mpart[i] = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int r = 0; r < 16; ++r) mpart[r % kAcc] = fmaxf(mpart[r % kAcc], s[kb][r]);
+      float mx = fmaxf(fmaxf(mpart[0], mpart[1]), fmaxf(mpart[2], mpart[3]));
       // The halves' maxima are exchanged only when some lane's maximum
       // exceeds the reference (the two halves hold keys of one query row).
       if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_ref) != 0) {
@@ -222,7 +230,8 @@ void fwd_fp8_kernel(FwdArgs a) {
         if (m_new > m_ref) {
           const float alpha = fast_exp2(m_ref - m_new);
           m_ref = m_new;
-          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < kAcc; ++i) l_part[i] *= alpha;
 #pragma unroll
           for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -236,7 +245,7 @@ void fwd_fp8_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(s[kb][r], sl2, kPShift - mu));
           s[kb][r] = p;
-          l_run += p;
+          l_part[r % kAcc] += p;
         }
       // P^T operand: byte 16kb + r of this lane = weight s[kb][r].
       i32x8 pb;
@@ -274,7 +283,7 @@ void fwd_fp8_kernel(FwdArgs a) {
   }
 
   // Epilogue: O = v_descale * acc / l (bf16), LSE in natural units.
-  const float l_tot = half_pair_sum(l_run);
+  const float l_tot = half_pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   const float inv = l_tot > 0.f ? a.v_descale / l_tot : 0.f;
   if (qrow < N) {
     if (h == 0)
