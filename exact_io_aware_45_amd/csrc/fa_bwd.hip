@@ -103,8 +103,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int nkt = (N + T::BK - 1) / T::BK;
   const int total = nkt * a.B * a.Hkv;
   const int w = xcd_remap(blockIdx.x, total);
-  const int bkv = w / nkt;  // K/V head b * Hkv + hk
-  const int kt = w % nkt;   // small key tiles see the most queries: first
+  int bkv = w / nkt;  // K/V head b * Hkv + hk
+  int kt = w % nkt;
+  if constexpr (CAUSAL) causal_order(w, total, nkt, bkv, kt);  // small key tiles see the most queries
   const int kt0 = kt * T::BK;
   const int G = a.H / a.Hkv;  // query heads per K/V head
   const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * G;  // the group's first query head
@@ -349,8 +350,12 @@ void bwd_dq_kernel(BwdArgs a) {
   const int nqt = (N + T::BQ - 1) / T::BQ;
   const int total = nqt * a.B * a.H;
   const int w = xcd_remap(blockIdx.x, total);
-  const int bh = w / nqt;
-  const int qt = CAUSAL ? (nqt - 1 - w % nqt) : (w % nqt);
+  int bh = w / nqt, qt = w % nqt;
+  if constexpr (CAUSAL) {  // heaviest (last) query tiles first
+    int rank;
+    causal_order(w, total, nqt, bh, rank);
+    qt = nqt - 1 - rank;
+  }
   const int q0 = qt * T::BQ;
 
   const int lane = threadIdx.x & 63;

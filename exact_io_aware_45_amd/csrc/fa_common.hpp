@@ -143,4 +143,22 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return (wg % kXcd) * per + wg / kXcd;
 }
 
+// Work item w (an xcd_remap output) of a grid of `total` items, `ntile` tiles
+// per head, for causal work whose cost falls with the tile's rank (rank 0 is
+// the heaviest).  When each XCD's share holds whole heads, the share is
+// ordered heaviest first across all its heads (every head's rank-0 tile, then
+// every head's rank-1 tile, ...), so that the light tiles fill the tail;
+// otherwise heaviest first within each head.
+__device__ __forceinline__ void causal_order(int w, int total, int ntile, int& head, int& rank) {
+  constexpr int kXcd = 8;
+  if (total % kXcd == 0 && (total / kXcd) % ntile == 0) {
+    const int per = total / kXcd, hpx = per / ntile, j = w % per;
+    head = (w / per) * hpx + j % hpx;
+    rank = j / hpx;
+  } else {
+    head = w / ntile;
+    rank = w % ntile;
+  }
+}
+
 }  // namespace fa

@@ -92,8 +92,12 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int nq = (N + kBR - 1) / kBR;
   const int total = nq * a.B * a.H;
   const int w = xcd_remap(blockIdx.x, total);
-  const int bh = w / nq;
-  const int qt = kIsCausal ? (nq - 1 - w % nq) : (w % nq);
+  int bh = w / nq, qt = w % nq;
+  if constexpr (kIsCausal) {  // heaviest (last) query tiles first
+    int rank;
+    causal_order(w, total, nq, bh, rank);
+    qt = nq - 1 - rank;
+  }
   const int q0 = qt * kBR;
 
   const int lane = threadIdx.x & 63;

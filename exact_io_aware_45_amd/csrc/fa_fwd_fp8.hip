@@ -113,8 +113,12 @@ void fwd_fp8_kernel(FwdArgs a) {
   const int nq = (N + BR - 1) / BR;
   const int total = nq * a.B * a.H;
   const int w = xcd_remap(blockIdx.x, total);
-  const int bh = w / nq;
-  const int qt = CAUSAL ? (nq - 1 - w % nq) : (w % nq);
+  int bh = w / nq, qt = w % nq;
+  if constexpr (CAUSAL) {  // heaviest (last) query tiles first
+    int rank;
+    causal_order(w, total, nq, bh, rank);
+    qt = nq - 1 - rank;
+  }
   const int q0 = qt * BR;
 
   const int lane = threadIdx.x & 63;
