@@ -86,14 +86,20 @@ __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, x, true);
 }
 
+// Four waves (128 query rows) per workgroup for both head sizes. d = 128 holds
+// about 165 VGPRs, so three workgroups share a CU (three waves per SIMD); that
+// leaves more waves to hide one wave's softmax behind another's MFMAs than two
+// 8-wave workgroups would. d = 64 fits four per SIMD.
+constexpr int kWaves = 4;
+
 template <int D>
-constexpr int kWaves = D == 128 ? 8 : 4;
+constexpr int kWavesPerSimd = D == 128 ? 3 : 4;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves<D>)
-__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 4, D == 128 ? 2 : 4)))
+__global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>)))
 void fwd_fp8_kernel(FwdArgs a) {
-  constexpr int NW = kWaves<D>;
+  constexpr int NW = kWaves;
   constexpr int kThreads = 64 * NW;
   constexpr int BR = 32 * NW;      // query rows per workgroup
   constexpr int BC = 64;           // keys per tile
@@ -308,15 +314,15 @@ void fwd_fp8_kernel(FwdArgs a) {
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-  constexpr int BR = 32 * kWaves<D>;
+  constexpr int BR = 32 * kWaves;
   const int nq = (a.N + BR - 1) / BR;
   const long long grid = (long long)nq * a.B * a.H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, true>), dim3((unsigned)grid), dim3(64 * kWaves<D>), 0, s,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0, s,
                        a);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, false>), dim3((unsigned)grid), dim3(64 * kWaves<D>), 0,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
                        s, a);
   return hipGetLastError();
 }
