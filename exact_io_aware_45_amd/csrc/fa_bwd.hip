@@ -19,12 +19,13 @@
 //
 // Three launches on the caller's stream, deterministic (no atomics):
 //   1. bwd_delta: D_i = dO_i . O_i (fp32), into the caller's workspace;
-//   2. bwd_dkdv:  one workgroup per 128 keys (d=128) or 256 keys (d=64); each
-//      wave keeps 32 keys' K and V
-//      in registers and loops over 64-query tiles of Q and dO staged in LDS:
-//      S = Q K^T and dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE),
-//      dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read from
-//      the row-major LDS tiles by transpose reads;
+//   2. bwd_dkdv:  one workgroup per 128 keys (d=128) or 256 keys (d=64) loops
+//      over 64-query tiles of Q and dO staged in LDS: S = Q K^T and
+//      dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE), dS, then
+//      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read from the
+//      row-major LDS tiles by transpose reads.  d=64: each wave owns 32 keys,
+//      K and V in registers.  d=128: two waves share 32 keys (K and V in LDS)
+//      and split each query tile, and their partial sums meet in LDS;
 //   3. bwd_dq:    one workgroup per 128 queries; each wave keeps 32 queries'
 //      Q and dO in registers and loops over 64-key tiles of K and V, staged in
 //      LDS by direct loads:
@@ -79,14 +80,10 @@ struct DkdvTile {
   static_assert(BQ * CH % THREADS == 0, "tile must split evenly");
 };
 
-// d=128 keeps fp32 dK/dV accumulators (128 registers) and the K/V operands
-// (64) resident: one wave per SIMD.  d=64 fits two.
-template <int D>
-constexpr int kDkdvWavesPerEU = D == 128 ? 1 : 2;
-
+// Used for d=64: fp32 dK/dV accumulators (64 registers) and the K/V operands
+// (32) stay resident at two waves per SIMD.
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(kDkdvWavesPerEU<D>, kDkdvWavesPerEU<D>)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D, NW>;
   constexpr bool CAUSAL = (MODE & kCausal) != 0;
@@ -235,8 +232,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         s = mfma32(lds_read8(Qs + off), kf[c], s);
         dp = mfma32(lds_read8(Os + off), vf[c], dp);
       }
-      // Issue order: operand reads two MFMAs ahead (one wave per SIMD leaves
-      // nothing else to hide LDS latency behind).
+      // Issue order: operand reads two MFMAs ahead.
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int i = 0; i < 2 * DC - 2; ++i) {
@@ -310,14 +306,269 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// dK, dV for d = 128: 8-wave workgroups of 128 keys.  Waves w and w + 4 own
+// the same 32 keys and take the two 32-query halves of every 64-query tile;
+// their partial dK/dV are summed through LDS at the end in a fixed order, so
+// the result stays deterministic.  K and V are read from an LDS copy instead
+// of being held as register operands, which brings a wave under 256 registers
+// (fp32 dK/dV accumulators 128, the rest about 110): two waves share a SIMD,
+// so one wave's exponentials overlap the other's matrix instructions.
+constexpr int kSplitKeys = 128;  // keys per workgroup (4 blocks of 32)
+
+template <int D, int MODE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_split_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = (MODE & kCausal) != 0;
+  constexpr bool SPARSE = (MODE & kSparse) != 0;
+  constexpr int NW = 8;
+  constexpr int BK = kSplitKeys;
+  constexpr int BQ = 64;   // queries per loop step (2 halves of 32)
+  constexpr int CH = D / 8;
+  constexpr int LOADS = BQ * CH / (64 * NW);     // direct loads per lane, Q or dO tile
+  constexpr int KV_LOADS = BK * CH / (64 * NW);  // direct loads per lane, K or V
+  constexpr int T_ELEMS = BQ * D;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  static_assert(BQ * CH % (64 * NW) == 0 && BK * CH % (64 * NW) == 0, "tiles must split evenly");
+  static_assert(BK * D * 2 * 2 >= 4 * 32 * D * 4, "the K/V copy holds one tensor's partials");
+
+  // One LDS array per tensor and stage.
+  __shared__ __attribute__((aligned(16))) bf16 q_s0[T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 q_s1[T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 o_s0[T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 o_s1[T_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 kv_s[2][BK * D];  // [K|V], swizzled rows
+  __shared__ __attribute__((aligned(16))) float l_s0[BQ];  // LSE rows of the tile
+  __shared__ __attribute__((aligned(16))) float l_s1[BQ];
+  __shared__ __attribute__((aligned(16))) float d_s0[BQ];  // D rows of the tile
+  __shared__ __attribute__((aligned(16))) float d_s1[BQ];
+
+  const int N = a.N;
+  const int nkt = (N + BK - 1) / BK;
+  const int total = nkt * a.B * a.Hkv;
+  const int w = xcd_remap(blockIdx.x, total);
+  int bkv = w / nkt;  // K/V head b * Hkv + hk
+  int kt = w % nkt;
+  if constexpr (CAUSAL) causal_order(w, total, nkt, bkv, kt);  // small key tiles see the most queries
+  const int kt0 = kt * BK;
+  const int G = a.H / a.Hkv;
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * G;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kw = wave & 3;   // this wave's 32-key block
+  const int qh = wave >> 2;  // this wave's 32-query half of every tile
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  const size_t head = (size_t)bkv * N * D;
+  const size_t qhead = (size_t)bq0 * N * D;
+  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + qhead;
+  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
+  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
+  const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + qhead;
+  const float* __restrict__ LSE = a.lse + (size_t)bq0 * N;
+  const float* __restrict__ DEL = a.delta + (size_t)bq0 * N;
+
+  const int key = kt0 + 32 * kw + l32;
+
+  // K and V of the workgroup's keys: HBM -> LDS direct loads, row r chunk q
+  // stored at chunk q ^ tile_swz(r) (rows past N repeat row N - 1).
+#pragma unroll
+  for (int i = 0; i < KV_LOADS; ++i) {
+    const int base = (i * NW + wave) * 64;
+    const int lp = base + lane;
+    const int row = lp / CH;
+    const int q = (lp % CH) ^ tile_swz<D>(row);
+    const size_t src = (size_t)min(kt0 + row, N - 1) * D + 8 * q;
+    lds_load16(K + src, &kv_s[0][8 * base]);
+    lds_load16(V + src, &kv_s[1][8 * base]);
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[b][r] = 0.f;
+      dv[b][r] = 0.f;
+    }
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt_begin = CAUSAL ? kt0 / BQ : 0;
+  const float sl2 = a.scale * kLog2e;
+
+  const uint8_t* mcol = nullptr;
+  int mb = 1, nmb = 1;
+  if constexpr (SPARSE) {
+    mb = a.mask_block;
+    nmb = (N + mb - 1) / mb;
+    mcol = a.mask + kt0 / mb;
+  }
+  struct Pos {
+    int g, qt;
+  };
+  auto advance = [&](Pos p) {  // the first visited (query head, query tile) at or after p
+    for (;;) {
+      if (p.qt >= nqt) {
+        p.qt = qt_begin;
+        ++p.g;
+      }
+      if (p.g >= G) return p;
+      if constexpr (SPARSE) {
+        if (mcol[(size_t)((p.qt * BQ) / mb) * nmb]) return p;
+        ++p.qt;
+      } else {
+        return p;
+      }
+    }
+  };
+
+  auto load_tile = [&](Pos p, bf16* Qd, bf16* Od, float* Ld, float* Dd) {
+    const size_t ho = (size_t)p.g * N * D;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int base = (i * NW + wave) * 64;
+      const int lp = base + lane;
+      const int row = lp / CH;
+      const int q = (lp % CH) ^ tile_swz<D>(row);
+      const size_t src = ho + (size_t)min(p.qt * BQ + row, N - 1) * D + 8 * q;
+      lds_load16(Q + src, Qd + 8 * base);
+      lds_load16(dO + src, Od + 8 * base);
+    }
+    const size_t qr = (size_t)p.g * N + min(p.qt * BQ + lane, N - 1);
+    if (wave == 0) lds_load4(LSE + qr, Ld);
+    if (wave == 1) lds_load4(DEL + qr, Dd);
+  };
+
+  // Row-wise reads: Q/dO row 32qh + l32 and K/V row 32kw + l32, chunk 2c + h
+  // (tile_swz depends on the row modulo 16 only, so one swizzle serves both).
+  const int sw_row = tile_swz<D>(l32);
+  const int qrow = (32 * qh + l32) * D;
+  const int krow = (32 * kw + l32) * D;
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
+  const int tq = tr_col >> 3, te = tr_col & 7;
+  auto tr_off = [&](int row, int sw, int b) {
+    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+  };
+
+  Pos cur = advance(Pos{0, qt_begin});
+  if (cur.g < G) load_tile(cur, q_s0, o_s0, l_s0, d_s0);
+  __syncthreads();  // K/V and the first tile resident
+
+  auto tile_step = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, bf16* Qn,
+                       bf16* On, float* Ln, float* Dn) {
+    const Pos nxt = advance(Pos{cur.g, cur.qt + 1});
+    if (nxt.g < G) load_tile(nxt, Qn, On, Ln, Dn);  // lands during this tile's math
+    const int q0 = cur.qt * BQ + 32 * qh;  // this wave's first query
+    // Skip a half that lies wholly above the diagonal or past N.
+    const bool empty = (CAUSAL && q0 + 31 < kt0 + 32 * kw) || q0 >= N;
+    if (!empty) {
+      const bool need_mask = (CAUSAL && q0 < kt0 + 32 * kw + 31) || (q0 + 32 > N);
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const int off = 8 * ((2 * c + h) ^ sw_row);
+        s = mfma32(lds_read8(Qs + qrow + off), lds_read8(&kv_s[0][krow + off]), s);
+        dp = mfma32(lds_read8(Os + qrow + off), lds_read8(&kv_s[1][krow + off]), dp);
+      }
+      // s[r], dp[r]: query q0 + 8(r/4) + 4h + r%4, key `key`.
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * qh + 8 * g + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
+          if (need_mask) {
+            const int q = q0 + 8 * g + 4 * h + e;
+            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[e]);
+        }
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over this half's queries)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 pb = pack8(s[8 * cc + 0], s[8 * cc + 1], s[8 * cc + 2], s[8 * cc + 3],
+                                s[8 * cc + 4], s[8 * cc + 5], s[8 * cc + 6], s[8 * cc + 7]);
+        const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
+                                dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
+        const int r_lo = 32 * qh + 16 * cc + tr_row;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const int o_lo = tr_off(r_lo, sw_lo, b), o_hi = tr_off(r_lo + 8, sw_hi, b);
+          dv[b] = mfma32(cat8(lds_read_tr4(Os + o_lo), lds_read_tr4(Os + o_hi)), pb, dv[b]);
+          dk[b] = mfma32(cat8(lds_read_tr4(Qs + o_lo), lds_read_tr4(Qs + o_hi)), db, dk[b]);
+        }
+      }
+    }
+    __syncthreads();  // also drains this wave's direct loads of the next tile
+    cur = nxt;
+  };
+  // The stage is a run-time select: a loop unrolled over both stages holds
+  // twice the LDS addresses and spills at 256 registers.
+  int stage = 0;
+  while (cur.g < G) {
+    tile_step(stage ? q_s1 : q_s0, stage ? o_s1 : o_s0, stage ? l_s1 : l_s0, stage ? d_s1 : d_s0,
+              stage ? q_s0 : q_s1, stage ? o_s0 : o_s1, stage ? l_s0 : l_s1, stage ? d_s0 : d_s1);
+    stage ^= 1;
+  }
+
+  // Sum the two halves' partials through the (no longer needed) K/V copy:
+  // wave 4 + kw's 16 KB of one tensor at float offset 4096 kw, lane-major.
+  // dK: the upper wave hands over, the lower one adds and stores; dV the other
+  // way round.  dK^T, dV^T lane layout: key `key`, d = 32b + 8(r/4) + 4h + r%4.
+  float* xs = reinterpret_cast<float*>(&kv_s[0][0]) + 4096 * kw;
+  auto put = [&](const f32x16* acc) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[b][4 * g + e];
+        *reinterpret_cast<f32x4*>(xs + 4 * ((4 * b + g) * 64 + lane)) = v4;
+      }
+  };
+  auto add_store = [&](const f32x16* acc, float* out, float mul) {
+    if (key >= N) return;
+    float* row = out + head + (size_t)key * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o4 = *reinterpret_cast<const f32x4*>(xs + 4 * ((4 * b + g) * 64 + lane));
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (acc[b][4 * g + e] + o4[e]) * mul;
+        *reinterpret_cast<f32x4*>(row + 32 * b + 8 * g + 4 * h) = v4;
+      }
+  };
+  if (qh == 1) put(dk);
+  __syncthreads();
+  if (qh == 0) add_store(dk, a.dk, a.scale);
+  __syncthreads();
+  if (qh == 0) put(dv);
+  __syncthreads();
+  if (qh == 1) add_store(dv, a.dv, 1.f);
+}
+
 // ---------------------------------------------------------------------- dQ
 // 4 waves, 32 queries per wave; 64-key tiles of K and V in swizzled LDS
 // tiles (K read row-wise for S^T = K Q^T and column-wise for dQ^T += K^T dS^T).
 #ifndef FA_DQ_BK128
 #define FA_DQ_BK128 64
-#endif
-#ifndef FA_DKDV_WAVES128
-#define FA_DKDV_WAVES128 4
 #endif
 
 template <int D>
@@ -505,22 +756,27 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// dK/dV workgroup size: d=128 needs about 300 registers per lane (one wave
-// per SIMD, 4 waves); d=64 fits two waves per SIMD (8 waves).  With a tile
-// mask the workgroup's 32 * NW keys must lie in one mask column: 4 waves.
+// dK/dV workgroup size for d=64: 8 waves (256 keys); with a tile mask the
+// workgroup's 32 * NW keys must lie in one mask column: 4 waves.  (d=128 uses
+// the 128-key split kernel in every mode.)
 template <int D, int MODE>
-constexpr int kDkdvWaves = (MODE & kSparse) ? 4 : (D == 128 ? FA_DKDV_WAVES128 : 8);
+constexpr int kDkdvWaves = (MODE & kSparse) ? 4 : 8;
 
 template <int D, int MODE>
 hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
   using TK = DkdvTile<D, kDkdvWaves<D, MODE>>;
-  static_assert(!(MODE & kSparse) || 128 % TK::BK == 0, "dK/dV keys must fit one mask tile");
+  constexpr int BK = D == 128 ? kSplitKeys : TK::BK;  // keys per dK/dV workgroup
+  static_assert(!(MODE & kSparse) || 128 % BK == 0, "dK/dV keys must fit one mask tile");
   static_assert(!(MODE & kSparse) || DqTile<D>::BQ == 128, "dQ rows must be one mask tile");
-  const long long g1 = (long long)((a.N + TK::BK - 1) / TK::BK) * a.B * a.Hkv;
+  const long long g1 = (long long)((a.N + BK - 1) / BK) * a.B * a.Hkv;
   const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D, MODE>, MODE>), dim3((unsigned)g1),
-                     dim3(TK::THREADS), 0, s, a);
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, MODE>), dim3((unsigned)g1), dim3(512), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D, MODE>, MODE>), dim3((unsigned)g1),
+                       dim3(TK::THREADS), 0, s, a);
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
