@@ -241,23 +241,28 @@ void bwd_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       // s[r], dp[r]: query 32qb + 8(r/4) + 4h + r%4 of this tile, key `key`.
+      // Masked and unmasked copies behind one wave-uniform branch.
+      auto probs = [&](auto masked) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 32 * qb + 8 * g + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[stage][ql]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[stage][ql]);
+        for (int g = 0; g < 4; ++g) {
+          const int ql = 32 * qb + 8 * g + 4 * h;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[stage][ql]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[stage][ql]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
-          if (need_mask) {
-            const int q = q0 + ql + e;
-            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
+            if constexpr (decltype(masked)::value) {
+              const int q = q0 + ql + e;
+              if (q >= N || (CAUSAL && key > q)) p = 0.f;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[e]);
           }
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[e]);
         }
-      }
+      };
+      if (need_mask) probs(std::true_type{});
+      else probs(std::false_type{});
       // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over this block's queries)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -311,9 +316,29 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // their partial dK/dV are summed through LDS at the end in a fixed order, so
 // the result stays deterministic.  K and V are read from an LDS copy instead
 // of being held as register operands, which brings a wave under 256 registers
-// (fp32 dK/dV accumulators 128, the rest about 110): two waves share a SIMD,
-// so one wave's exponentials overlap the other's matrix instructions.
+// (fp32 dK/dV accumulators 128, S and dP 32, loop-invariant LDS offsets 25):
+// two waves share a SIMD, so one wave's exponentials overlap the other's
+// matrix instructions.  LDS is one hand-laid-out array, so that every operand
+// read is a loop-invariant offset register plus an immediate.
 constexpr int kSplitKeys = 128;  // keys per workgroup (4 blocks of 32)
+
+// Direct HBM -> LDS copies issued as inline assembly: the compiler does not
+// track them, so it inserts no wait for them before LDS reads; the kernel
+// waits (vmcnt) before the barrier that publishes each tile.
+__device__ __forceinline__ void dma16_untracked(const void* src, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_untracked(const void* src, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
 
 template <int D, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -322,42 +347,36 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
   constexpr bool SPARSE = (MODE & kSparse) != 0;
   constexpr int NW = 8;
   constexpr int BK = kSplitKeys;
-  constexpr int BQ = 64;   // queries per loop step (2 halves of 32)
+  constexpr int BQ = 64;
   constexpr int CH = D / 8;
-  constexpr int LOADS = BQ * CH / (64 * NW);     // direct loads per lane, Q or dO tile
-  constexpr int KV_LOADS = BK * CH / (64 * NW);  // direct loads per lane, K or V
-  constexpr int T_ELEMS = BQ * D;
+  constexpr int LOADS = BQ * CH / (64 * NW);
+  constexpr int KV_LOADS = BK * CH / (64 * NW);
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
-  static_assert(BQ * CH % (64 * NW) == 0 && BK * CH % (64 * NW) == 0, "tiles must split evenly");
-  static_assert(BK * D * 2 * 2 >= 4 * 32 * D * 4, "the K/V copy holds one tensor's partials");
-
-  // One LDS array per tensor and stage.
-  __shared__ __attribute__((aligned(16))) bf16 q_s0[T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 q_s1[T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 o_s0[T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 o_s1[T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 kv_s[2][BK * D];  // [K|V], swizzled rows
-  __shared__ __attribute__((aligned(16))) float l_s0[BQ];  // LSE rows of the tile
-  __shared__ __attribute__((aligned(16))) float l_s1[BQ];
-  __shared__ __attribute__((aligned(16))) float d_s0[BQ];  // D rows of the tile
-  __shared__ __attribute__((aligned(16))) float d_s1[BQ];
+  static_assert(D == 128, "byte layout below is for d = 128");
+  // LDS byte layout: stage s at 32 KB s = [Q tile 16 KB | dO tile 16 KB];
+  // K at 64 KB, V at 96 KB (32 KB each); LSE, D rows of stage s at
+  // 128 KB + 512 s (+256 for D).  Stage offsets and the dO / V / D
+  // displacements are compile-time constants that fold into the reads'
+  // immediate offsets.
+  constexpr unsigned kStage = 32768, kDO = 16384, kK = 65536, kV = 32768, kRows = 131072;
+  __shared__ __attribute__((aligned(16))) char lds[kRows + 1024];
 
   const int N = a.N;
   const int nkt = (N + BK - 1) / BK;
   const int total = nkt * a.B * a.Hkv;
   const int w = xcd_remap(blockIdx.x, total);
-  int bkv = w / nkt;  // K/V head b * Hkv + hk
+  int bkv = w / nkt;
   int kt = w % nkt;
-  if constexpr (CAUSAL) causal_order(w, total, nkt, bkv, kt);  // small key tiles see the most queries
+  if constexpr (CAUSAL) causal_order(w, total, nkt, bkv, kt);
   const int kt0 = kt * BK;
   const int G = a.H / a.Hkv;
   const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * G;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int kw = wave & 3;   // this wave's 32-key block
-  const int qh = wave >> 2;  // this wave's 32-query half of every tile
+  const int kw = wave & 3;
+  const int qh = wave >> 2;
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -369,11 +388,10 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
   const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + qhead;
   const float* __restrict__ LSE = a.lse + (size_t)bq0 * N;
   const float* __restrict__ DEL = a.delta + (size_t)bq0 * N;
+  const unsigned lds0 = (unsigned)(size_t)(FA_LDS void*)lds;
 
   const int key = kt0 + 32 * kw + l32;
 
-  // K and V of the workgroup's keys: HBM -> LDS direct loads, row r chunk q
-  // stored at chunk q ^ tile_swz(r) (rows past N repeat row N - 1).
 #pragma unroll
   for (int i = 0; i < KV_LOADS; ++i) {
     const int base = (i * NW + wave) * 64;
@@ -381,8 +399,8 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
     const int row = lp / CH;
     const int q = (lp % CH) ^ tile_swz<D>(row);
     const size_t src = (size_t)min(kt0 + row, N - 1) * D + 8 * q;
-    lds_load16(K + src, &kv_s[0][8 * base]);
-    lds_load16(V + src, &kv_s[1][8 * base]);
+    dma16_untracked(K + src, lds0 + kK + 16 * base);
+    dma16_untracked(V + src, lds0 + kK + kV + 16 * base);
   }
 
   f32x16 dk[DB], dv[DB];
@@ -408,7 +426,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
   struct Pos {
     int g, qt;
   };
-  auto advance = [&](Pos p) {  // the first visited (query head, query tile) at or after p
+  auto advance = [&](Pos p) {
     for (;;) {
       if (p.qt >= nqt) {
         p.qt = qt_begin;
@@ -424,7 +442,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
     }
   };
 
-  auto load_tile = [&](Pos p, bf16* Qd, bf16* Od, float* Ld, float* Dd) {
+  auto load_tile = [&](Pos p, unsigned st) {
     const size_t ho = (size_t)p.g * N * D;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -433,37 +451,57 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
       const int row = lp / CH;
       const int q = (lp % CH) ^ tile_swz<D>(row);
       const size_t src = ho + (size_t)min(p.qt * BQ + row, N - 1) * D + 8 * q;
-      lds_load16(Q + src, Qd + 8 * base);
-      lds_load16(dO + src, Od + 8 * base);
+      dma16_untracked(Q + src, lds0 + st * kStage + 16 * base);
+      dma16_untracked(dO + src, lds0 + st * kStage + kDO + 16 * base);
     }
     const size_t qr = (size_t)p.g * N + min(p.qt * BQ + lane, N - 1);
-    if (wave == 0) lds_load4(LSE + qr, Ld);
-    if (wave == 1) lds_load4(DEL + qr, Dd);
+    if (wave == 0) dma4_untracked(LSE + qr, lds0 + kRows + 512 * st);
+    if (wave == 1) dma4_untracked(DEL + qr, lds0 + kRows + 512 * st + 256);
   };
 
-  // Row-wise reads: Q/dO row 32qh + l32 and K/V row 32kw + l32, chunk 2c + h
-  // (tile_swz depends on the row modulo 16 only, so one swizzle serves both).
+  // Loop-invariant per-lane byte offsets.  Row-wise reads: row 32qh + l32 of
+  // the Q tile (K: row 32kw + l32), chunk (2c + h) ^ tile_swz(l32).
   const int sw_row = tile_swz<D>(l32);
-  const int qrow = (32 * qh + l32) * D;
-  const int krow = (32 * kw + l32) * D;
+  unsigned qoff[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) qoff[c] = (32 * qh + l32) * D * 2 + 16 * ((2 * c + h) ^ sw_row);
+  // K rows sit a wave-uniform distance from this wave's Q rows (one scalar
+  // add per K read instead of 8 more offset registers).
+  unsigned kdelta = __builtin_amdgcn_readfirstlane(kK + 64 * D * (kw - qh));
+  // Transpose reads: rows 32qh + 16cc + tr_row (+8), chunk 4b + (tr_col >> 3),
+  // element tr_col & 7; the cc term is a constant 16-row step.
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
   const int tq = tr_col >> 3, te = tr_col & 7;
-  auto tr_off = [&](int row, int sw, int b) {
-    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+  unsigned troff[DB][2];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    troff[b][0] = 2 * ((32 * qh + tr_row) * D + 8 * (((4 * b) ^ (sw_lo & 12)) | (tq ^ (sw_lo & 3))) + te);
+    troff[b][1] = 2 * ((32 * qh + tr_row + 8) * D + 8 * (((4 * b) ^ (sw_hi & 12)) | (tq ^ (sw_hi & 3))) + te);
+  }
+  const unsigned rowoff = kRows + 4 * (32 * qh + 4 * h);
+
+  auto rd8 = [&](unsigned off) { return *(const FA_LDS bf16x8*)(lds + off); };
+  auto rdtr = [&](unsigned off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(lds + off));
+    return __builtin_bit_cast(bf16x4, r);
   };
 
   Pos cur = advance(Pos{0, qt_begin});
-  if (cur.g < G) load_tile(cur, q_s0, o_s0, l_s0, d_s0);
+  if (cur.g < G) load_tile(cur, 0);
+  wait_global_loads();
   __syncthreads();  // K/V and the first tile resident
 
-  auto tile_step = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, bf16* Qn,
-                       bf16* On, float* Ln, float* Dn) {
+  unsigned st = 0;  // current stage
+  auto tile_step = [&]() {
+    // so: byte offset of the current stage, loop-carried so that the
+    // compiler cannot hoist one address register per stage out of the loop.
+    const unsigned so = st * kStage;
+    asm volatile("" : "+s"(kdelta));  // opaque per step, so K addresses are not hoisted
     const Pos nxt = advance(Pos{cur.g, cur.qt + 1});
-    if (nxt.g < G) load_tile(nxt, Qn, On, Ln, Dn);  // lands during this tile's math
-    const int q0 = cur.qt * BQ + 32 * qh;  // this wave's first query
-    // Skip a half that lies wholly above the diagonal or past N.
+    if (nxt.g < G) load_tile(nxt, st ^ 1);
+    const int q0 = cur.qt * BQ + 32 * qh;
     const bool empty = (CAUSAL && q0 + 31 < kt0 + 32 * kw) || q0 >= N;
     if (!empty) {
       const bool need_mask = (CAUSAL && q0 < kt0 + 32 * kw + 31) || (q0 + 32 > N);
@@ -475,61 +513,63 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const int off = 8 * ((2 * c + h) ^ sw_row);
-        s = mfma32(lds_read8(Qs + qrow + off), lds_read8(&kv_s[0][krow + off]), s);
-        dp = mfma32(lds_read8(Os + qrow + off), lds_read8(&kv_s[1][krow + off]), dp);
+        const unsigned qa = qoff[c] + so;
+        const unsigned ka = qoff[c] + kdelta;
+        s = mfma32(rd8(qa), rd8(ka), s);
+        dp = mfma32(rd8(qa + kDO), rd8(ka + kV), dp);
       }
-      // s[r], dp[r]: query q0 + 8(r/4) + 4h + r%4, key `key`.
+      auto probs = [&](auto masked) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 32 * qh + 8 * g + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + ql);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *(const FA_LDS f32x4*)(lds + rowoff + st * 512 + 32 * g);
+          const f32x4 d4 = *(const FA_LDS f32x4*)(lds + rowoff + st * 512 + 256 + 32 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
-          if (need_mask) {
-            const int q = q0 + 8 * g + 4 * h + e;
-            if (q >= N || (CAUSAL && key > q)) p = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
+            if constexpr (decltype(masked)::value) {
+              const int q = q0 + 8 * g + 4 * h + e;
+              if (q >= N || (CAUSAL && key > q)) p = 0.f;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[e]);
           }
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[e]);
         }
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over this half's queries)
+      };
+      if (need_mask) probs(std::true_type{});
+      else probs(std::false_type{});
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const bf16x8 pb = pack8(s[8 * cc + 0], s[8 * cc + 1], s[8 * cc + 2], s[8 * cc + 3],
                                 s[8 * cc + 4], s[8 * cc + 5], s[8 * cc + 6], s[8 * cc + 7]);
         const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
                                 dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
-        const int r_lo = 32 * qh + 16 * cc + tr_row;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const int o_lo = tr_off(r_lo, sw_lo, b), o_hi = tr_off(r_lo + 8, sw_hi, b);
-          dv[b] = mfma32(cat8(lds_read_tr4(Os + o_lo), lds_read_tr4(Os + o_hi)), pb, dv[b]);
-          dk[b] = mfma32(cat8(lds_read_tr4(Qs + o_lo), lds_read_tr4(Qs + o_hi)), db, dk[b]);
+          const unsigned lo = troff[b][0] + so + 16 * D * 2 * cc;
+          const unsigned hi = troff[b][1] + so + 16 * D * 2 * cc;
+          dv[b] = mfma32(cat8(rdtr(lo + kDO), rdtr(hi + kDO)), pb, dv[b]);
+          dk[b] = mfma32(cat8(rdtr(lo), rdtr(hi)), db, dk[b]);
         }
       }
+      // Transposed operand reads one MFMA ahead.  (The same order for the S
+      // and dP products costs registers the kernel does not have.)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DB - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __syncthreads();  // also drains this wave's direct loads of the next tile
+    wait_global_loads();
+    __syncthreads();  // the next tile is resident; this one may be overwritten
     cur = nxt;
+    st ^= 1;
   };
-  // The stage is a run-time select: a loop unrolled over both stages holds
-  // twice the LDS addresses and spills at 256 registers.
-  int stage = 0;
-  while (cur.g < G) {
-    tile_step(stage ? q_s1 : q_s0, stage ? o_s1 : o_s0, stage ? l_s1 : l_s0, stage ? d_s1 : d_s0,
-              stage ? q_s0 : q_s1, stage ? o_s0 : o_s1, stage ? l_s0 : l_s1, stage ? d_s0 : d_s1);
-    stage ^= 1;
-  }
+  while (cur.g < G) tile_step();
 
-  // Sum the two halves' partials through the (no longer needed) K/V copy:
-  // wave 4 + kw's 16 KB of one tensor at float offset 4096 kw, lane-major.
-  // dK: the upper wave hands over, the lower one adds and stores; dV the other
-  // way round.  dK^T, dV^T lane layout: key `key`, d = 32b + 8(r/4) + 4h + r%4.
-  float* xs = reinterpret_cast<float*>(&kv_s[0][0]) + 4096 * kw;
+  float* xs = reinterpret_cast<float*>(lds + kK) + 4096 * kw;
   auto put = [&](const f32x16* acc) {
 #pragma unroll
     for (int b = 0; b < DB; ++b)
@@ -709,16 +749,21 @@ void bwd_dq_kernel(BwdArgs a) {
         s = mfma32(lds_read8(Ks + off), qf[c], s);
         dp = mfma32(lds_read8(Vs + off), of[c], dp);
       }
-      // s[r], dp[r]: key k0 + 32kb + 8(r/4) + 4h + r%4, query qrow.
+      // s[r], dp[r]: key k0 + 32kb + 8(r/4) + 4h + r%4, query qrow.  Masked
+      // and unmasked copies behind one wave-uniform branch.
+      auto grads = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], sl2, -lse2));
-        if (need_mask) {
-          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(s[r], sl2, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+          }
+          dp[r] = p * (dp[r] - dlt);
         }
-        dp[r] = p * (dp[r] - dlt);
-      }
+      };
+      if (need_mask) grads(std::true_type{});
+      else grads(std::false_type{});
       // dQ^T += K^T dS^T (contraction over this block's keys)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
