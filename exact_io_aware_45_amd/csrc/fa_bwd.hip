@@ -749,6 +749,14 @@ void bwd_dq_kernel(BwdArgs a) {
         s = mfma32(lds_read8(Ks + off), qf[c], s);
         dp = mfma32(lds_read8(Vs + off), of[c], dp);
       }
+      // Issue order: each operand read one MFMA ahead of its use.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DC - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       // s[r], dp[r]: key k0 + 32kb + 8(r/4) + 4h + r%4, query qrow.  Masked
       // and unmasked copies behind one wave-uniform branch.
       auto grads = [&](auto masked) {
@@ -777,6 +785,13 @@ void bwd_dq_kernel(BwdArgs a) {
           dq[b] = mfma32(ka, db, dq[b]);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DB - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     __syncthreads();  // also drains this wave's direct loads of tile tn
     t = tn;
