@@ -332,6 +332,22 @@ __device__ __forceinline__ void dma16_untracked(const void* src, unsigned lds_by
                : "v"(src), "s"(m0)
                : "memory", "m0");
 }
+// Same, with a wave-uniform base address in scalar registers and a 32-bit
+// per-lane byte offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16_sbase(const void* base, unsigned off, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_sbase(const void* base, unsigned off, unsigned lds_byte) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4_untracked(const void* src, unsigned lds_byte) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -442,8 +458,29 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
     }
   };
 
+  // Per-lane byte offsets of the direct loads within a whole tile.
+  unsigned loff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lp = (i * NW + wave) * 64 + lane;
+    const int row = lp / CH;
+    loff[i] = 2 * (row * D + 8 * ((lp % CH) ^ tile_swz<D>(row)));
+  }
   auto load_tile = [&](Pos p, unsigned st) {
     const size_t ho = (size_t)p.g * N * D;
+    if ((p.qt + 1) * BQ <= N) {  // whole tile in range: scalar base + lane offsets
+      const size_t t0 = ho + (size_t)p.qt * BQ * D;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const unsigned dst = lds0 + st * kStage + 16 * ((i * NW + wave) * 64);
+        dma16_sbase(Q + t0, loff[i], dst);
+        dma16_sbase(dO + t0, loff[i], dst + kDO);
+      }
+      const size_t r0 = (size_t)p.g * N + (size_t)p.qt * BQ;
+      if (wave == 0) dma4_sbase(LSE + r0, 4 * lane, lds0 + kRows + 512 * st);
+      if (wave == 1) dma4_sbase(DEL + r0, 4 * lane, lds0 + kRows + 512 * st + 256);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int base = (i * NW + wave) * 64;
@@ -631,11 +668,13 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int DB = D / 32;
   constexpr int NB = T::BK / 32;
 
-  // One LDS array per tensor and stage (see tile_step).
-  __shared__ __attribute__((aligned(16))) bf16 k_s0[T::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 k_s1[T::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 v_s0[T::T_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 v_s1[T::T_ELEMS];
+  // LDS byte layout: stage s at kStage * s = [K tile | V tile].  The stage
+  // is a loop-carried byte offset and the V, key-block and cc displacements
+  // are immediates, so each operand read is one offset register plus an
+  // immediate.
+  constexpr unsigned kTile = T::T_ELEMS * 2, kStage = 2 * kTile;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+  const unsigned lds0 = (unsigned)(size_t)(FA_LDS void*)lds;
 
   const int N = a.N;
   const int nqt = (N + T::BQ - 1) / T::BQ;
@@ -701,7 +740,24 @@ void bwd_dq_kernel(BwdArgs a) {
   // HBM -> LDS direct loads of one key tile of K and V (chunk q of row r at
   // chunk q ^ tile_swz(r)): lane l of a wave's i-th load fills LDS position
   // p = (i * 4 + wave) * 64 + l, i.e. row p / CH, slot p % CH.
-  auto load_tile = [&](int t, bf16* Kd, bf16* Vd) {
+  unsigned loff[T::LOADS];
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;
+    const int row = p / T::CH;
+    loff[i] = 2 * (row * D + 8 * ((p % T::CH) ^ tile_swz<D>(row)));
+  }
+  auto load_tile = [&](int t, unsigned st) {
+    if ((t + 1) * T::BK <= N) {  // whole tile in range: scalar base + lane offsets
+      const size_t t0 = (size_t)t * T::BK * D;
+#pragma unroll
+      for (int i = 0; i < T::LOADS; ++i) {
+        const unsigned dst = lds0 + st * kStage + 16 * ((i * 4 + wave) * 64);
+        dma16_sbase(K + t0, loff[i], dst);
+        dma16_sbase(V + t0, loff[i], dst + kTile);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int base = (i * 4 + wave) * 64;
@@ -709,29 +765,47 @@ void bwd_dq_kernel(BwdArgs a) {
       const int row = p / T::CH;
       const int q = (p % T::CH) ^ tile_swz<D>(row);
       const size_t src = (size_t)min(t * T::BK + row, N - 1) * D + 8 * q;
-      lds_load16(K + src, Kd + 8 * base);
-      lds_load16(V + src, Vd + 8 * base);
+      dma16_untracked(K + src, lds0 + st * kStage + 16 * base);
+      dma16_untracked(V + src, lds0 + st * kStage + kTile + 16 * base);
     }
   };
 
+  // Loop-invariant per-lane byte offsets: row-wise reads of row l32, chunk
+  // (2c + h) ^ tile_swz(l32); transpose reads of rows tr_row (+8), chunk
+  // 4b + (tr_col >> 3), element tr_col & 7.  The key block (32 rows), cc
+  // (16 rows), V and stage terms are added as constants or once per step.
   const int sw_row = tile_swz<D>(l32);
+  unsigned roff[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) roff[c] = 2 * (l32 * D + 8 * ((2 * c + h) ^ sw_row));
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
   const int tq = tr_col >> 3, te = tr_col & 7;
-  auto tr_off = [&](int row, int sw, int b) {
-    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+  unsigned troff[DB][2];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    troff[b][0] = 2 * (tr_row * D + 8 * (((4 * b) ^ (sw_lo & 12)) | (tq ^ (sw_lo & 3))) + te);
+    troff[b][1] = 2 * ((tr_row + 8) * D + 8 * (((4 * b) ^ (sw_hi & 12)) | (tq ^ (sw_hi & 3))) + te);
+  }
+  auto rd8 = [&](unsigned off) { return *(const FA_LDS bf16x8*)(lds + off); };
+  auto rdtr = [&](unsigned off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(lds + off));
+    return __builtin_bit_cast(bf16x4, r);
   };
 
   wait_global_loads();  // Q, dO operands resident before the key loop
   int t = next_tile(0);
-  if (t < tend) load_tile(t, k_s0, v_s0);
+  if (t < tend) load_tile(t, 0);
+  wait_global_loads();
   __syncthreads();
-  // One key tile: computes with (Ks, Vs) while the next visited tile lands in
-  // (Kn, Vn).
-  auto tile_step = [&](const bf16* Ks, const bf16* Vs, bf16* Kn, bf16* Vn) {
+  unsigned st = 0;
+  // One key tile: computes with stage st while the next visited tile lands in
+  // the other stage.
+  auto tile_step = [&]() {
+    const unsigned so = st * kStage;
     const int tn = next_tile(t + 1);
-    if (tn < tend) load_tile(tn, Kn, Vn);
+    if (tn < tend) load_tile(tn, st ^ 1);
     const int k0 = t * T::BK;
     const bool need_mask = (CAUSAL && k0 + T::BK - 1 > q0 + 32 * wave) || (k0 + T::BK > N);
 #pragma unroll
@@ -742,12 +816,11 @@ void bwd_dq_kernel(BwdArgs a) {
         s[r] = 0.f;
         dp[r] = 0.f;
       }
-      const int rrow = (32 * kb + l32) * D;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const int off = rrow + 8 * ((2 * c + h) ^ sw_row);
-        s = mfma32(lds_read8(Ks + off), qf[c], s);
-        dp = mfma32(lds_read8(Vs + off), of[c], dp);
+        const unsigned off = roff[c] + so + 2 * 32 * D * kb;
+        s = mfma32(rd8(off), qf[c], s);
+        dp = mfma32(rd8(off + kTile), of[c], dp);
       }
       // Issue order: each operand read one MFMA ahead of its use.
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -777,11 +850,10 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int cc = 0; cc < 2; ++cc) {
         const bf16x8 db = pack8(dp[8 * cc + 0], dp[8 * cc + 1], dp[8 * cc + 2], dp[8 * cc + 3],
                                 dp[8 * cc + 4], dp[8 * cc + 5], dp[8 * cc + 6], dp[8 * cc + 7]);
-        const int r_lo = 32 * kb + 16 * cc + tr_row;
+        const unsigned rb = so + 2 * (32 * kb + 16 * cc) * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const bf16x8 ka = cat8(lds_read_tr4(Ks + tr_off(r_lo, sw_lo, b)),
-                                 lds_read_tr4(Ks + tr_off(r_lo + 8, sw_hi, b)));
+          const bf16x8 ka = cat8(rdtr(troff[b][0] + rb), rdtr(troff[b][1] + rb));
           dq[b] = mfma32(ka, db, dq[b]);
         }
       }
@@ -793,14 +865,12 @@ void bwd_dq_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    __syncthreads();  // also drains this wave's direct loads of tile tn
+    wait_global_loads();
+    __syncthreads();  // the next tile is resident; this one may be overwritten
     t = tn;
+    st ^= 1;
   };
-  int stage = 0;
-  while (t < tend) {
-    tile_step(stage ? k_s1 : k_s0, stage ? v_s1 : v_s0, stage ? k_s0 : k_s1, stage ? v_s0 : v_s1);
-    stage ^= 1;
-  }
+  while (t < tend) tile_step();
 
   if (qrow < N) {
     float* dqrow = a.dq + head + (size_t)qrow * D;
