@@ -60,7 +60,7 @@ size_t workspace_size(int B, int H, int N, int d) {
   bool empty = false;
   if (check_shape(B, H, N, d, 1.0f, &empty) != FA_OK || empty) return 0;
   const size_t rows = (size_t)B * H * N;
-  return (rows * sizeof(float) + 255) / 256 * 256;
+  return (2 * rows * sizeof(float) + 255) / 256 * 256;  // D, then LSE * log2(e)
 }
 
 int backward_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -80,7 +80,8 @@ int backward_common(const void* q, const void* k, const void* v, const void* o, 
     return FA_ERR_INVALID_ARG;
   fa::BwdArgs a{q,  k,  v,  o,     dout,           lse,  dq,         dk, dv,
                 static_cast<float*>(workspace), B, H, N, d, scale, causal ? 1 : 0,
-                mask, mask_block, Hkv};
+                mask, mask_block, Hkv, nullptr};
+  a.lse2 = a.delta + (size_t)B * H * N;
   (void)hipGetLastError();
   return hip_status(fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -18,7 +18,8 @@
 // both passes: the dQ pass walks its mask row, the dK/dV pass its mask column.
 //
 // Three launches on the caller's stream, deterministic (no atomics):
-//   1. bwd_delta: D_i = dO_i . O_i (fp32), into the caller's workspace;
+//   1. bwd_delta: D_i = dO_i . O_i and LSE_i * log2(e) (fp32), into the
+//      caller's workspace;
 //   2. bwd_dkdv:  one workgroup per 128 keys (d=128) or 256 keys (d=64) loops
 //      over 64-query tiles of Q and dO staged in LDS: S = Q K^T and
 //      dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE), dS, then
@@ -62,7 +63,10 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a, long lon
   }
 #pragma unroll
   for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
-  if (row < rows && ch == 0) a.delta[row] = acc;
+  if (row < rows && ch == 0) {
+    a.delta[row] = acc;
+    a.lse2[row] = a.lse[row] * kLog2e;  // the dK/dV and dQ passes' exponent offset
+  }
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -118,7 +122,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
   const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
   const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + qhead;
-  const float* __restrict__ LSE = a.lse + (size_t)bq0 * N;
+  const float* __restrict__ LSE2 = a.lse2 + (size_t)bq0 * N;  // LSE * log2(e)
   const float* __restrict__ DEL = a.delta + (size_t)bq0 * N;
 
   // This wave's keys as B operands: K^T for S = Q K^T, V^T for dP = dO V^T.
@@ -188,7 +192,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       lds_load16(dO + src, &tiles[st][1][8 * base]);
     }
     const size_t qr = (size_t)p.g * N + min(p.qt * T::BQ + lane, N - 1);
-    if (wave == 0) lds_load4(LSE + qr, &lse_s[st][0]);
+    if (wave == 0) lds_load4(LSE2 + qr, &lse_s[st][0]);
     if (wave == 1) lds_load4(DEL + qr, &del_s[st][0]);
   };
 
@@ -251,7 +255,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
+            float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
             if constexpr (decltype(masked)::value) {
               const int q = q0 + ql + e;
               if (q >= N || (CAUSAL && key > q)) p = 0.f;
@@ -371,7 +375,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
   constexpr int DB = D / 32;
   static_assert(D == 128, "byte layout below is for d = 128");
   // LDS byte layout: stage s at 32 KB s = [Q tile 16 KB | dO tile 16 KB];
-  // K at 64 KB, V at 96 KB (32 KB each); LSE, D rows of stage s at
+  // K at 64 KB, V at 96 KB (32 KB each); LSE * log2(e), D rows of stage s at
   // 128 KB + 512 s (+256 for D).  Stage offsets and the dO / V / D
   // displacements are compile-time constants that fold into the reads'
   // immediate offsets.
@@ -402,7 +406,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
   const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + head;
   const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + head;
   const bf16* __restrict__ dO = reinterpret_cast<const bf16*>(a.dout) + qhead;
-  const float* __restrict__ LSE = a.lse + (size_t)bq0 * N;
+  const float* __restrict__ LSE2 = a.lse2 + (size_t)bq0 * N;  // LSE * log2(e)
   const float* __restrict__ DEL = a.delta + (size_t)bq0 * N;
   const unsigned lds0 = (unsigned)(size_t)(FA_LDS void*)lds;
 
@@ -477,7 +481,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
         dma16_sbase(dO + t0, loff[i], dst + kDO);
       }
       const size_t r0 = (size_t)p.g * N + (size_t)p.qt * BQ;
-      if (wave == 0) dma4_sbase(LSE + r0, 4 * lane, lds0 + kRows + 512 * st);
+      if (wave == 0) dma4_sbase(LSE2 + r0, 4 * lane, lds0 + kRows + 512 * st);
       if (wave == 1) dma4_sbase(DEL + r0, 4 * lane, lds0 + kRows + 512 * st + 256);
       return;
     }
@@ -492,7 +496,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
       dma16_untracked(dO + src, lds0 + st * kStage + kDO + 16 * base);
     }
     const size_t qr = (size_t)p.g * N + min(p.qt * BQ + lane, N - 1);
-    if (wave == 0) dma4_untracked(LSE + qr, lds0 + kRows + 512 * st);
+    if (wave == 0) dma4_untracked(LSE2 + qr, lds0 + kRows + 512 * st);
     if (wave == 1) dma4_untracked(DEL + qr, lds0 + kRows + 512 * st + 256);
   };
 
@@ -563,7 +567,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float p = fast_exp2(fmaf(s[r], sl2, -l4[e] * kLog2e));
+            float p = fast_exp2(fmaf(s[r], sl2, -l4[e]));
             if constexpr (decltype(masked)::value) {
               const int q = q0 + 8 * g + 4 * h + e;
               if (q >= N || (CAUSAL && key > q)) p = 0.f;
@@ -709,7 +713,7 @@ void bwd_dq_kernel(BwdArgs a) {
     qf[c] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qld * D + 16 * c + 8 * h);
     of[c] = *reinterpret_cast<const bf16x8*>(dO + (size_t)qld * D + 16 * c + 8 * h);
   }
-  const float lse2 = a.lse[(size_t)bh * N + qld] * kLog2e;
+  const float lse2 = a.lse2[(size_t)bh * N + qld];
   const float dlt = a.delta[(size_t)bh * N + qld];
   const float sl2 = a.scale * kLog2e;
 

@@ -42,6 +42,7 @@ struct BwdArgs {
   const uint8_t* mask;  // tile mask [nmb][nmb] or nullptr
   int mask_block;
   int Hkv;  // K, V, dK, dV are [B][Hkv][N][d]; dK/dV sum over the H/Hkv query heads
+  float* lse2;  // workspace: LSE_i * log2(e), [B][H][N] fp32 (written with D)
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

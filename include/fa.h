@@ -69,8 +69,10 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
                    int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * Bytes of device workspace fa_backward needs for this shape (the per-row
- * D_i = dO_i . O_i, fp32 [B][H][N]).  Returns 0 for empty or invalid shapes.
+ * Bytes of device workspace fa_backward needs for this shape: two fp32
+ * [B][H][N] arrays, the per-row D_i = dO_i . O_i and LSE_i * log2(e), which
+ * the first launch writes and the other two read.  Returns 0 for empty or
+ * invalid shapes.
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 

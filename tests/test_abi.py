@@ -105,7 +105,7 @@ def test_blocksparse_argument_errors():
 
 def test_backward_workspace_and_argument_errors():
     lib = _lib.load()
-    assert _lib.backward_workspace_size(4, 16, 4096, 128) == 4 * 16 * 4096 * 4
+    assert _lib.backward_workspace_size(4, 16, 4096, 128) == 2 * 4 * 16 * 4096 * 4
     assert _lib.backward_workspace_size(1, 1, 3, 64) == 256
     assert _lib.backward_workspace_size(1, 1, 0, 64) == 0
     assert _lib.backward_workspace_size(1, 1, 16, 80) == 0
