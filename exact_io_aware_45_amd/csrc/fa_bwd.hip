@@ -20,8 +20,8 @@
 // Three launches on the caller's stream, deterministic (no atomics):
 //   1. bwd_delta: D_i = dO_i . O_i and LSE_i * log2(e) (fp32), into the
 //      caller's workspace;
-//   2. bwd_dkdv:  one workgroup per 128 keys (d=128) or 256 keys (d=64) loops
-//      over 64-query tiles of Q and dO staged in LDS: S = Q K^T and
+//   2. bwd_dkdv:  one workgroup per 128 keys loops over 64-query tiles of Q
+//      and dO staged in LDS: S = Q K^T and
 //      dP = dO V^T on MFMA (lane = key column), P = exp(S - LSE), dS, then
 //      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read from the
 //      row-major LDS tiles by transpose reads.  d=64: each wave owns 32 keys,
@@ -85,7 +85,7 @@ struct DkdvTile {
 };
 
 // Used for d=64: fp32 dK/dV accumulators (64 registers) and the K/V operands
-// (32) stay resident at two waves per SIMD.
+// (32) stay resident at two waves per SIMD; 4-wave workgroups.
 template <int D, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
@@ -890,11 +890,12 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// dK/dV workgroup size for d=64: 8 waves (256 keys); with a tile mask the
-// workgroup's 32 * NW keys must lie in one mask column: 4 waves.  (d=128 uses
-// the 128-key split kernel in every mode.)
+// dK/dV workgroup size for d=64: 4 waves (128 keys) in every mode, so that a
+// tile mask's 128-key column is one workgroup and short sequences still give
+// two workgroups per CU (4 % faster than 8 waves at B8 H16 N1024 causal).
+// (d=128 uses the 128-key split kernel in every mode.)
 template <int D, int MODE>
-constexpr int kDkdvWaves = (MODE & kSparse) ? 4 : 8;
+constexpr int kDkdvWaves = 4;
 
 template <int D, int MODE>
 hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
