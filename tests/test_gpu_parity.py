@@ -103,6 +103,18 @@ def test_forward_full_workloads(name):
         forward_parity(x["q"], x["k"], x["v"], w.causal, sample_pairs(w.B, w.H, 4, seed))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 50, 64, 65, 128, 129, 192, 200, 333, 600])
+def test_forward_eight_wave_grid(N, causal):
+    """Enough heads (B4 H130) that the launch takes 8-wave workgroups (the
+    long-sequence configuration) at short, ragged N: 1, 2, 3, ... key tiles
+    per workgroup, so the K/V staging ring starts and ends at every phase."""
+    need_gpu()
+    log(f"forward bf16 B4 H130 N{N} d128 causal={causal} (8-wave grid)")
+    q, k, v = inputs.qkv(4, 130, N, 128, torch.bfloat16, seed=1000 + N)
+    forward_parity(q, k, v, causal, sample_pairs(4, 130, 6, seed=N))
+
+
 def test_causal_row_zero_is_v0_exactly():
     need_gpu()
     q, k, v = inputs.qkv(2, 2, 300, 128, torch.bfloat16, seed=3)
