@@ -129,12 +129,24 @@ def _mask(block_mask, N, mask_block):
         raise ValueError(f"block_mask must be a contiguous uint8 device tensor [{nb}][{nb}]")
 
 
+def _fwd_out(q, B, H, N, odtype, out):
+    """(o, lse): new tensors, or the caller's `out` pair after checking it."""
+    if out is None:
+        return (torch.empty(q.shape, dtype=odtype, device=q.device),
+                torch.empty((B, H, N), dtype=torch.float32, device=q.device))
+    o, lse = out
+    _tensor("o", o, odtype, q.shape)
+    _tensor("lse", lse, torch.float32, (B, H, N))
+    return o, lse
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None):
-    """fa_forward (bf16) or fa_forward_f32 (fp32). Returns (o, lse)."""
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+    """fa_forward (bf16) or fa_forward_f32 (fp32). Returns (o, lse), written into
+    `out` = (o, lse) when given (o like q, lse fp32 [B,H,N])."""
     lib = load()
     if q.dtype == torch.float32:
         B, H, _, N, d = _shape(q, k, v, torch.float32)
@@ -142,21 +154,19 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None):
     else:
         B, H, _, N, d = _shape(q, k, v, torch.bfloat16)
         fn, what = lib.fa_forward, "fa_forward"
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, lse = _fwd_out(q, B, H, N, q.dtype, out)
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
               int(bool(causal)), _stream(q.device)), what)
     return o, lse
 
 
 def forward_blocksparse(q, k, v, block_mask, mask_block: int = 128, causal: bool = False,
-                        scale: float | None = None):
+                        scale: float | None = None, out=None):
     """fa_forward_blocksparse: block_mask is a uint8 device tensor [nb][nb]."""
     lib = load()
     B, H, _, N, d = _shape(q, k, v, torch.bfloat16)
     _mask(block_mask, N, mask_block)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, lse = _fwd_out(q, B, H, N, q.dtype, out)
     _check(lib.fa_forward_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                       _scale(scale, d), int(bool(causal)), _ptr(block_mask),
                                       int(mask_block), _stream(q.device)),
@@ -164,12 +174,11 @@ def forward_blocksparse(q, k, v, block_mask, mask_block: int = 128, causal: bool
     return o, lse
 
 
-def forward_gqa(q, k, v, causal: bool = False, scale: float | None = None):
+def forward_gqa(q, k, v, causal: bool = False, scale: float | None = None, out=None):
     """fa_forward_gqa: q [B,H,N,d], k, v [B,Hkv,N,d] bf16 (Hkv divides H)."""
     lib = load()
     B, H, Hkv, N, d = _shape(q, k, v, torch.bfloat16, grouped=True)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, lse = _fwd_out(q, B, H, N, q.dtype, out)
     _check(lib.fa_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
                               _scale(scale, d), int(bool(causal)), _stream(q.device)),
            "fa_forward_gqa")
@@ -177,12 +186,11 @@ def forward_gqa(q, k, v, causal: bool = False, scale: float | None = None):
 
 
 def forward_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
-                causal: bool = False, scale: float | None = None):
+                causal: bool = False, scale: float | None = None, out=None):
     """fa_forward_fp8: q, k, v torch.float8_e4m3fn [B,H,N,d] codes; returns (o bf16, lse)."""
     lib = load()
     B, H, _, N, d = _shape(q, k, v, torch.float8_e4m3fn)
-    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, lse = _fwd_out(q, B, H, N, torch.bfloat16, out)
     _check(lib.fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                               _scale(scale, d), float(q_descale), float(k_descale),
                               float(v_descale), int(bool(causal)), _stream(q.device)),
@@ -194,7 +202,7 @@ def backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load().fa_backward_workspace_size(B, H, N, d))
 
 
-def _backward_args(q, k, v, o, dout, lse, grouped, workspace):
+def _backward_args(q, k, v, o, dout, lse, grouped, workspace, out=None):
     B, H, Hkv, N, d = _shape(q, k, v, torch.bfloat16, grouped)
     _tensor("o", o, torch.bfloat16, q.shape)
     _tensor("dout", dout, torch.bfloat16, q.shape)
@@ -204,16 +212,22 @@ def _backward_args(q, k, v, o, dout, lse, grouped, workspace):
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     else:
         _tensor("workspace", workspace, torch.uint8)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    dk, dv = (torch.empty(k.shape, dtype=torch.float32, device=q.device) for _ in range(2))
+    if out is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk, dv = (torch.empty(k.shape, dtype=torch.float32, device=q.device) for _ in range(2))
+    else:
+        dq, dk, dv = out
+        _tensor("dq", dq, torch.float32, q.shape)
+        _tensor("dk", dk, torch.float32, k.shape)
+        _tensor("dv", dv, torch.float32, k.shape)
     return (B, H, Hkv, N, d), workspace, (dq, dk, dv)
 
 
 def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
-             workspace=None):
+             workspace=None, out=None):
     """fa_backward: returns (dq, dk, dv), fp32."""
     lib = load()
-    (B, H, _, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, False, workspace)
+    (B, H, _, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, False, workspace, out)
     _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                            _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H, N, d,
                            _scale(scale, d), int(bool(causal)), _stream(q.device)),
@@ -222,10 +236,11 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
 
 
 def backward_blocksparse(q, k, v, o, dout, lse, block_mask, mask_block: int = 128,
-                         causal: bool = False, scale: float | None = None, workspace=None):
+                         causal: bool = False, scale: float | None = None, workspace=None,
+                         out=None):
     """fa_backward_blocksparse: the gradients of fa_forward_blocksparse, fp32."""
     lib = load()
-    (B, H, _, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, False, workspace)
+    (B, H, _, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, False, workspace, out)
     _mask(block_mask, N, mask_block)
     _check(lib.fa_backward_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H,
@@ -236,10 +251,10 @@ def backward_blocksparse(q, k, v, o, dout, lse, block_mask, mask_block: int = 12
 
 
 def backward_gqa(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
-                 workspace=None):
+                 workspace=None, out=None):
     """fa_backward_gqa: dq [B,H,N,d]; dk, dv [B,Hkv,N,d] summed over each group, fp32."""
     lib = load()
-    (B, H, Hkv, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, True, workspace)
+    (B, H, Hkv, N, d), ws, (dq, dk, dv) = _backward_args(q, k, v, o, dout, lse, True, workspace, out)
     _check(lib.fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H, Hkv, N,
                                d, _scale(scale, d), int(bool(causal)), _stream(q.device)),

@@ -115,6 +115,27 @@ def test_forward_eight_wave_grid(N, causal):
     forward_parity(q, k, v, causal, sample_pairs(4, 130, 6, seed=N))
 
 
+def test_caller_outputs_match_fresh_outputs():
+    """forward/backward with caller-owned output buffers (out=) write exactly
+    what they return with fresh ones, also over stale contents."""
+    need_gpu()
+    q, k, v, do = (t.to(DEV) for t in inputs.qkv(2, 3, 200, 128, torch.bfloat16, seed=5,
+                                                  with_dout=True))
+    o, lse = _lib.forward(q, k, v, causal=True)
+    fo = (torch.full_like(o, 7.0), torch.full_like(lse, -3.0))
+    ro = _lib.forward(q, k, v, causal=True, out=fo)
+    g = _lib.backward(q, k, v, o, do, lse, causal=True)
+    bo = tuple(torch.full_like(x, 11.0) for x in g)
+    rb = _lib.backward(q, k, v, o, do, lse, causal=True, out=bo)
+    torch.cuda.synchronize()
+    assert ro[0] is fo[0] and ro[1] is fo[1] and all(x is y for x, y in zip(rb, bo))
+    assert torch.equal(fo[0], o) and torch.equal(fo[1], lse)
+    for x, y in zip(bo, g):
+        assert torch.equal(x, y)
+    with pytest.raises(ValueError):
+        _lib.forward(q, k, v, out=(fo[0].float(), fo[1]))
+
+
 def test_causal_row_zero_is_v0_exactly():
     need_gpu()
     q, k, v = inputs.qkv(2, 2, 300, 128, torch.bfloat16, seed=3)
