@@ -136,6 +136,36 @@ def test_caller_outputs_match_fresh_outputs():
         _lib.forward(q, k, v, out=(fo[0].float(), fo[1]))
 
 
+def test_caller_outputs_other_entry_points():
+    """out= on the tile-mask, grouped-head and fp8 entry points."""
+    need_gpu()
+    q, k, v, do = (t.to(DEV) for t in inputs.qkv(1, 4, 300, 64, torch.bfloat16, seed=6,
+                                                  with_dout=True))
+    mask = inputs.block_mask(300, 128, 1, 0.5, 6).to(DEV)
+    calls = [
+        (lambda out=None: _lib.forward_blocksparse(q, k, v, mask, causal=True, out=out)),
+        (lambda out=None: _lib.forward_gqa(q, k[:, :2].contiguous(), v[:, :2].contiguous(),
+                                           causal=False, out=out)),
+    ]
+    f8 = inputs.qkv_fp8(1, 4, 300, 64, 6)
+    q8, k8, v8 = (x[0].to(DEV) for x in f8)
+    calls.append(lambda out=None: _lib.forward_fp8(q8, k8, v8, *(x[1] for x in f8),
+                                                   causal=True, out=out))
+    for fn in calls:
+        o, lse = fn()
+        buf = (torch.full_like(o, 5.0), torch.full_like(lse, 2.0))
+        fn(out=buf)
+        torch.cuda.synchronize()
+        assert torch.equal(buf[0], o) and torch.equal(buf[1], lse)
+    o, lse = _lib.forward_blocksparse(q, k, v, mask, causal=True)
+    g = _lib.backward_blocksparse(q, k, v, o, do, lse, mask, causal=True)
+    bo = tuple(torch.full_like(x, 3.0) for x in g)
+    _lib.backward_blocksparse(q, k, v, o, do, lse, mask, causal=True, out=bo)
+    torch.cuda.synchronize()
+    for x, y in zip(bo, g):
+        assert torch.equal(x, y)
+
+
 def test_causal_row_zero_is_v0_exactly():
     need_gpu()
     q, k, v = inputs.qkv(2, 2, 300, 128, torch.bfloat16, seed=3)
