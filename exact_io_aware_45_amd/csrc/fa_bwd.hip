@@ -158,6 +158,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     nmb = (N + mb - 1) / mb;
     mcol = a.mask + kt0 / mb;
   }
+  MaskScan mscan(mcol, nmb, SPARSE ? nmb : 0);  // this workgroup's mask column
   struct Pos {
     int g, qt;
   };
@@ -169,8 +170,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
       }
       if (p.g >= G) return p;
       if constexpr (SPARSE) {
-        if (mcol[(size_t)((p.qt * T::BQ) / mb) * nmb]) return p;
-        ++p.qt;
+        const int blk = (p.qt * T::BQ) / mb;
+        const int vb = mscan.next(blk);
+        if (vb == blk) return p;
+        p.qt = (vb * mb) / T::BQ;  // first query tile of that block, or past the end
       } else {
         return p;
       }
@@ -443,6 +446,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
     nmb = (N + mb - 1) / mb;
     mcol = a.mask + kt0 / mb;
   }
+  MaskScan mscan(mcol, nmb, SPARSE ? nmb : 0);  // this workgroup's mask column
   struct Pos {
     int g, qt;
   };
@@ -454,8 +458,10 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
       }
       if (p.g >= G) return p;
       if constexpr (SPARSE) {
-        if (mcol[(size_t)((p.qt * BQ) / mb) * nmb]) return p;
-        ++p.qt;
+        const int blk = (p.qt * BQ) / mb;
+        const int vb = mscan.next(blk);
+        if (vb == blk) return p;
+        p.qt = (vb * mb) / BQ;  // first query tile of that block, or past the end
       } else {
         return p;
       }
@@ -728,15 +734,19 @@ void bwd_dq_kernel(BwdArgs a) {
   const int tend = CAUSAL ? min(nt, qmax / T::BK + 1) : nt;
   // With a tile mask, key tiles whose entry in this workgroup's mask row is 0
   // are skipped (BQ equals the mask tile, BK divides it).
-  const uint8_t* mrow = nullptr;
-  int mb = 1;
-  if constexpr (SPARSE) {
-    mb = a.mask_block;
-    mrow = a.mask + (size_t)(q0 / mb) * ((N + mb - 1) / mb);
-  }
+  // Tile mask: this workgroup's row, over the blocks that cover [0, tend).
+  const int mb = SPARSE ? a.mask_block : 1;
+  const int nmb = (N + mb - 1) / mb;
+  MaskScan mscan(SPARSE ? a.mask + (size_t)(q0 / mb) * nmb : nullptr, 1,
+                 SPARSE ? (tend * T::BK + mb - 1) / mb : 0);
+  // The first visited key tile at or after t (>= tend when none is left).
   auto next_tile = [&](int t) {
     if constexpr (SPARSE) {
-      while (t < tend && !mrow[(t * T::BK) / mb]) ++t;
+      if (t < tend) {
+        const int blk = (t * T::BK) / mb;
+        const int vb = mscan.next(blk);
+        if (vb != blk) t = (vb * mb) / T::BK;  // first tile of that block (BK divides mb)
+      }
     }
     return t;
   };

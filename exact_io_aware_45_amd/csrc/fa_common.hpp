@@ -134,6 +134,40 @@ __device__ __forceinline__ int tile_swz(int r) {
   else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// The visible entries of one row or column of a tile mask (entry i at
+// base[i * stride], i < n, nonzero = visible), read 64 entries at a time: one
+// byte load per lane and a wave vote give a wave-uniform bitmask, so finding
+// the next visible entry is a bit scan rather than a chain of dependent byte
+// loads (each a full memory round trip).  Every lane of the wave must call
+// next() together.
+struct MaskScan {
+  const uint8_t* base;
+  long long stride;
+  int n;
+  int chunk;       // first entry of the cached 64 (a multiple of 64), -1: none
+  uint64_t bits;   // bit j: entry chunk + j is visible
+
+  __device__ MaskScan(const uint8_t* b, long long st, int count)
+      : base(b), stride(st), n(count), chunk(-1), bits(0) {}
+
+  // The first visible entry at or after i, or n if there is none.
+  __device__ __forceinline__ int next(int i) {
+    while (i < n) {
+      const int c = i & ~63;
+      if (c != chunk) {
+        const int e = c + (int)(threadIdx.x & 63);
+        const bool on = e < n && base[(size_t)e * stride] != 0;
+        bits = __builtin_amdgcn_ballot_w64(on);
+        chunk = c;
+      }
+      const uint64_t rest = bits >> (i - c);
+      if (rest != 0) return i + (int)__builtin_ctzll(rest);
+      i = c + 64;
+    }
+    return n;
+  }
+};
+
 // Workgroup index -> work item, so that consecutive items stay on one XCD
 // (the hardware deals workgroups to the 8 XCDs round-robin; each XCD has its
 // own L2, and items of one head reuse the same K/V).  Falls back to identity

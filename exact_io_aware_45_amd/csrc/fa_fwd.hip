@@ -126,16 +126,19 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int nt = (N + BC - 1) / BC;
   const int qmax = min(q0 + kBR, N) - 1;
   const int tend = kIsCausal ? min(nt, qmax / BC + 1) : nt;
-  const uint8_t* mrow = nullptr;
-  int mb = 1;
-  if constexpr (kIsSparse) {
-    mb = a.mask_block;
-    const int nmb = (N + mb - 1) / mb;
-    mrow = a.mask + (size_t)(q0 / mb) * nmb;
-  }
+  // Tile mask: this workgroup's row, over the blocks that cover [0, tend).
+  const int mb = kIsSparse ? a.mask_block : 1;
+  const int nmb = (N + mb - 1) / mb;
+  MaskScan mscan(kIsSparse ? a.mask + (size_t)(q0 / mb) * nmb : nullptr, 1,
+                 kIsSparse ? (tend * BC + mb - 1) / mb : 0);
+  // The first visited tile at or after t (>= tend when none is left).
   auto next_tile = [&](int t) {
     if constexpr (kIsSparse) {
-      while (t < tend && !mrow[(t * BC) / mb]) ++t;
+      if (t < tend) {
+        const int blk = (t * BC) / mb;
+        const int vb = mscan.next(blk);
+        if (vb != blk) t = (vb * mb) / BC;  // first tile of that block (BC divides mb)
+      }
     }
     return t;
   };
