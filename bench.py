@@ -70,12 +70,14 @@ def flops(w, which: str, mask=None) -> float:
 def traffic_bytes(w, which: str) -> float:
     """Algorithmic HBM bytes of one call: read the inputs once, write the outputs once."""
     es = {"f32": 4.0, "fp8": 1.0}.get(w.dtype, 2.0)
-    t = w.B * w.H * w.N * w.d * es   # one input-dtype tensor
+    t = w.B * w.H * w.N * w.d * es   # one input-dtype tensor with the query heads
+    tkv = t * w.kv_heads / w.H       # K or V (fewer heads when grouped)
     to = w.B * w.H * w.N * w.d * (4.0 if w.dtype == "f32" else 2.0)  # O (bf16 unless fp32)
     rows = w.B * w.H * w.N * 4.0     # one fp32 [B,H,N] vector
     if which == "fwd":
-        return 3 * t + to + rows                # Q K V in, O + LSE out
-    return 5 * t + rows + 3 * 2 * t + 2 * rows  # Q K V O dO + LSE in; fp32 dQ dK dV out; D out/in
+        return t + 2 * tkv + to + rows  # Q K V in, O + LSE out
+    # Q K V O dO + LSE in; fp32 dQ dK dV out; D out/in
+    return 3 * t + 2 * tkv + rows + 2 * t + 2 * 2 * tkv + 2 * rows
 
 
 KERNEL_SOURCES = {
@@ -112,13 +114,15 @@ def cpu_baseline(w, inp, passes, mask=None, budget_s: float = 15.0, max_heads: i
     threads = oracle.max_threads()
     m = None if mask is None else mask.cpu().numpy()
     kw = {} if m is None else {"block_mask": m, "mask_block": w.mask_block}
+    G = w.H // w.kv_heads  # query heads per K/V head
     done, t_total = 0, 0.0
     while done < min(max_heads, w.B * w.H) and t_total < budget_s:
         b, h = divmod(done, w.H)
         t0 = time.perf_counter()
-        oracle.forward(q[b, h], k[b, h], v[b, h], w.scale, w.causal, **kw)
+        oracle.forward(q[b, h], k[b, h // G], v[b, h // G], w.scale, w.causal, **kw)
         if "bwd" in passes:
-            oracle.backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal, **kw)
+            oracle.backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], w.scale, w.causal,
+                            **kw)
         t_total += time.perf_counter() - t0
         done += 1
     per_head = sum(flops(w, p, mask) for p in passes) / (w.B * w.H)
@@ -208,6 +212,9 @@ def main():
                          "the inputs are not served from the 256 MB last-level cache")
     ap.add_argument("--fp8", action="store_true",
                     help="fp8 (OCP e4m3) inputs through fa_forward_fp8, forward only")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="grouped K/V heads: run a dense bf16 workload through fa_forward_gqa "
+                         "(and fa_backward_gqa) with this many K/V heads")
     args = ap.parse_args()
 
     if args.mfma_ceiling:
@@ -240,6 +247,13 @@ def main():
             sys.exit(2)
         w = dataclasses.replace(w, dtype="fp8")
         passes = ("fwd",)
+    if args.kv_heads:
+        if (w.dtype != "bf16" or w.sparse or args.fp8 or args.kv_heads < 1
+                or w.H % args.kv_heads):
+            print(json.dumps({"error": "--kv-heads takes a dense bf16 workload and a divisor "
+                                       "of its head count"}))
+            sys.exit(2)
+        w = dataclasses.replace(w, Hkv=args.kv_heads)
     if w.dtype == "f32" and "bwd" in passes:
         print(json.dumps({"error": "the fp32 path is forward only"}))
         sys.exit(2)
@@ -266,6 +280,9 @@ def main():
     else:
         host = inputs.qkv(w.B, w.H, w.N, w.d, w.torch_dtype, args.seed, with_dout=True)
         inp = dict(zip(("q", "k", "v", "dout"), host))
+        if w.Hkv:  # K, V with their own head count, from the next seed
+            _, inp["k"], inp["v"] = inputs.qkv(w.B, w.Hkv, w.N, w.d, w.torch_dtype,
+                                               args.seed + 1)
         q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
     mask = None
     if w.sparse:
@@ -279,19 +296,23 @@ def main():
     fout = (torch.empty(q.shape, dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
                         device=dev),
             torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
-    bout = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    bout = tuple(torch.empty(x.shape, dtype=torch.float32, device=dev) for x in (q, k, v))
 
     def fwd():
         if w.dtype == "fp8":
             return _lib.forward_fp8(q, k, v, *descales, causal=w.causal, out=fout)
         if maskd is not None:
             return _lib.forward_blocksparse(q, k, v, maskd, causal=w.causal, out=fout)
+        if w.Hkv:
+            return _lib.forward_gqa(q, k, v, causal=w.causal, out=fout)
         return _lib.forward(q, k, v, causal=w.causal, out=fout)
 
     def bwd(o, lse):
         if maskd is not None:
             _lib.backward_blocksparse(q, k, v, o, do, lse, maskd, causal=w.causal, workspace=ws,
                                       out=bout)
+        elif w.Hkv:
+            _lib.backward_gqa(q, k, v, o, do, lse, causal=w.causal, workspace=ws, out=bout)
         else:
             _lib.backward(q, k, v, o, do, lse, causal=w.causal, workspace=ws, out=bout)
 
@@ -337,7 +358,7 @@ def main():
 
     # Counter-measured bytes exist only for the default workload's kernels.
     traffic = (load_traffic(args.traffic_json)
-               if w.name == "long_d128_causal" and w.dtype == "bf16" else {})
+               if w.name == "long_d128_causal" and w.dtype == "bf16" and not w.Hkv else {})
 
     mode = ("block-sparse " if w.sparse else "") + ("causal" if w.causal else "non-causal")
     nw = 4 if w.sparse else 8
@@ -347,8 +368,9 @@ def main():
         fwd_kernel = (f"fwd_fp8_kernel<d={w.d}, BC=64, {8 if w.d == 128 else 4} waves, {mode}> "
                       "(1 launch per fa_forward_fp8)")
     else:
+        entry = "_blocksparse" if w.sparse else ("_gqa" if w.Hkv else "")
         fwd_kernel = (f"fwd_bf16_kernel<d={w.d}, BC=64, {nw} waves, {mode}> "
-                      f"(1 launch per fa_forward{'_blocksparse' if w.sparse else ''})")
+                      f"(1 launch per fa_forward{entry})")
     props = torch.cuda.get_device_properties(dev)
     peak = mfma_peak(w)
     line = {
@@ -374,6 +396,8 @@ def main():
                 "frac_of_peak": round(fwd_tf / peak, 4), "flops": ff},
         "roofline": roofline(w, "fwd", fwd_ms, ff, traffic.get("fwd_bf16_kernel"), fwd_kernel),
     }
+    if w.Hkv:
+        line["config"]["Hkv"] = w.Hkv
     if w.sparse:
         line["config"]["mask"] = {"tiles": int(mask.sum()), "of": int(mask.numel()),
                                   "block": w.mask_block, "band": w.band,
@@ -386,7 +410,7 @@ def main():
                        "frac_of_peak": round(bwd_tf / peak, 4), "flops": fb}
         line["roofline_bwd"] = roofline(
             w, "bwd", bwd_ms, fb, traffic.get("fa_backward"),
-            f"fa_backward{'_blocksparse' if w.sparse else ''} call = bwd_delta + bwd_dkdv + "
+            f"fa_backward{entry if w.dtype == 'bf16' else ''} call = bwd_delta + bwd_dkdv + "
             "bwd_dq launches")
     line["device"] = {"name": props.name, "cus": props.multi_processor_count,
                       "hip_runtime": _lib.runtime_version(), "libfa": _lib.version()}

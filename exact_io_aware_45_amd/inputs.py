@@ -39,6 +39,11 @@ class Workload:
     band: int = 1
     density: float = 0.125
     mask_block: int = 128
+    Hkv: int = 0  # K/V heads (grouped-head runs); 0: one per query head
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:

@@ -54,3 +54,19 @@ def test_fp8_traffic_and_peak():
     t = 32 * 8192 * 128
     assert bench.traffic_bytes(w, "fwd") == 3 * t + 2 * t + 32 * 8192 * 4
     assert bench.mfma_peak(w) == 2 * bench.PEAK_BF16_TFLOPS
+
+
+def test_grouped_head_traffic():
+    """K and V (and dK, dV) carry Hkv heads; Q, O, dO, dQ and the row vectors H."""
+    w = inputs.WORKLOADS["long_d128_causal"]
+    g = dataclasses.replace(w, Hkv=8)
+    t = 32 * 8192 * 128 * 2.0   # one bf16 tensor with 32 heads
+    kv = t / 4                  # with 8 heads
+    rows = 32 * 8192 * 4.0
+    assert g.kv_heads == 8 and w.kv_heads == 32
+    assert bench.traffic_bytes(g, "fwd") == 2 * t + 2 * kv + rows
+    # Q, O, dO (bf16) + K, V (bf16) + LSE in; dQ (fp32, H heads), dK, dV (fp32, Hkv) out;
+    # D written and read.
+    assert bench.traffic_bytes(g, "bwd") == 3 * t + 2 * kv + rows + 2 * t + 4 * kv + 2 * rows
+    assert bench.traffic_bytes(w, "bwd") == 5 * t + rows + 6 * t + 2 * rows
+    assert bench.flops(g, "fwd") == bench.flops(w, "fwd")
