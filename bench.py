@@ -288,8 +288,9 @@ def main():
     if w.sparse:
         mask = inputs.block_mask(w.N, w.mask_block, w.band, w.density, args.seed)
     maskd = None if mask is None else mask.to(dev)
-    ws = torch.empty(max(1, _lib.backward_workspace_size(w.B, w.H, w.N, w.d)), dtype=torch.uint8,
-                     device=dev)
+    ws_bytes = (_lib.backward_gqa_workspace_size(w.B, w.H, w.Hkv, w.N, w.d) if w.Hkv
+                else _lib.backward_workspace_size(w.B, w.H, w.N, w.d))
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
 
     # Outputs are allocated once, outside the timed region, as a serving loop
     # would reuse them: the timed calls are argument checks plus launches.

@@ -19,8 +19,8 @@ LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(_HERE, "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 SYMBOLS = ("fa_forward", "fa_forward_f32", "fa_backward_workspace_size", "fa_backward",
            "fa_forward_blocksparse", "fa_backward_blocksparse", "fa_forward_gqa",
-           "fa_backward_gqa", "fa_forward_fp8", "fa_error_string", "fa_version",
-           "fa_runtime_version")
+           "fa_backward_gqa", "fa_backward_gqa_workspace_size", "fa_forward_fp8",
+           "fa_error_string", "fa_version", "fa_runtime_version")
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load():
     lib.fa_forward_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
+    lib.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_backward_gqa_workspace_size.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
     lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i,
                                             i, f, i, vp, i, vp]
@@ -202,12 +204,17 @@ def backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load().fa_backward_workspace_size(B, H, N, d))
 
 
+def backward_gqa_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    return int(load().fa_backward_gqa_workspace_size(B, H, Hkv, N, d))
+
+
 def _backward_args(q, k, v, o, dout, lse, grouped, workspace, out=None):
     B, H, Hkv, N, d = _shape(q, k, v, torch.bfloat16, grouped)
     _tensor("o", o, torch.bfloat16, q.shape)
     _tensor("dout", dout, torch.bfloat16, q.shape)
     _tensor("lse", lse, torch.float32, (B, H, N))
-    ws_bytes = backward_workspace_size(B, H, N, d)
+    ws_bytes = (backward_gqa_workspace_size(B, H, Hkv, N, d) if grouped
+                else backward_workspace_size(B, H, N, d))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     else:

@@ -63,6 +63,29 @@ size_t workspace_size(int B, int H, int N, int d) {
   return (2 * rows * sizeof(float) + 255) / 256 * 256;  // D, then LSE * log2(e)
 }
 
+// Grouped-head backward: every dK/dV workgroup covers 128 keys of one K/V
+// head, so with few K/V heads the grid is small (MQA at B1 N8192: 64
+// workgroups for 256 CUs).  Each group's query heads are then split into S
+// slices (the smallest divisor of H / Hkv that gives 512 workgroups, else
+// H / Hkv), each writing fp32 partial dK/dV that a reduction sums in order.
+constexpr int kDkdvKeys = 128;
+constexpr long long kDkdvWorkgroups = 512;
+
+int gqa_slices(int B, int H, int Hkv, int N) {
+  const int G = H / Hkv;
+  const long long base = (long long)((N + kDkdvKeys - 1) / kDkdvKeys) * B * Hkv;
+  for (int sl = 1; sl < G; ++sl)
+    if (G % sl == 0 && base * sl >= kDkdvWorkgroups) return sl;
+  return G;
+}
+
+// Extra workspace bytes for the slices' partials (0 when there is one slice).
+size_t gqa_part_bytes(int B, int H, int Hkv, int N, int d) {
+  const int S = gqa_slices(B, H, Hkv, N);
+  if (S <= 1) return 0;
+  return 256 + 2 * (size_t)S * B * Hkv * N * d * sizeof(float);  // + alignment slack
+}
+
 int backward_common(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, float* dq, float* dk, float* dv, void* workspace,
                     size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
@@ -80,8 +103,16 @@ int backward_common(const void* q, const void* k, const void* v, const void* o, 
     return FA_ERR_INVALID_ARG;
   fa::BwdArgs a{q,  k,  v,  o,     dout,           lse,  dq,         dk, dv,
                 static_cast<float*>(workspace), B, H, N, d, scale, causal ? 1 : 0,
-                mask, mask_block, Hkv, nullptr};
+                mask, mask_block, Hkv, nullptr, 1, nullptr};
   a.lse2 = a.delta + (size_t)B * H * N;
+  if (Hkv != H) {
+    const size_t base = workspace_size(B, H, N, d), part = gqa_part_bytes(B, H, Hkv, N, d);
+    if (part > 0 && workspace_bytes >= base + part) {
+      const uintptr_t p = (reinterpret_cast<uintptr_t>(workspace) + base + 255) & ~uintptr_t(255);
+      a.gsplit = gqa_slices(B, H, Hkv, N);
+      a.part = reinterpret_cast<float*>(p);
+    }
+  }
   (void)hipGetLastError();
   return hip_status(fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -146,6 +177,13 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   return workspace_size(B, H, N, d);
+}
+
+size_t fa_backward_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, 1.0f, &empty) != FA_OK || empty) return 0;
+  if (check_groups(H, Hkv) != FA_OK) return 0;
+  return workspace_size(B, H, N, d) + gqa_part_bytes(B, H, Hkv, N, d);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -102,14 +102,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nkt = (N + T::BK - 1) / T::BK;
-  const int total = nkt * a.B * a.Hkv;
+  const int total = nkt * a.B * a.Hkv * a.gsplit;
   const int w = xcd_remap(blockIdx.x, total);
-  int bkv = w / nkt;  // K/V head b * Hkv + hk
+  int bkv = w / nkt;  // (K/V head b * Hkv + hk) * gsplit + slice
   int kt = w % nkt;
   if constexpr (CAUSAL) causal_order(w, total, nkt, bkv, kt);  // small key tiles see the most queries
+  const int slice = bkv % a.gsplit;
+  bkv /= a.gsplit;
   const int kt0 = kt * T::BK;
-  const int G = a.H / a.Hkv;  // query heads per K/V head
-  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * G;  // the group's first query head
+  const int G = a.H / a.Hkv / a.gsplit;  // query heads of this slice
+  // The slice's first query head.
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * (a.H / a.Hkv) + slice * G;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -300,8 +303,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   // dK^T, dV^T (fp32 out): lane holds key `key`, d = 32b + 8(r/4) + 4h + r%4.
   if (key < N) {
-    float* dkrow = a.dk + head + (size_t)key * D;
-    float* dvrow = a.dv + head + (size_t)key * D;
+    const size_t kvsize = (size_t)a.B * a.Hkv * N * D;
+    float* dkrow = (a.gsplit > 1 ? a.part + slice * kvsize : a.dk) + head + (size_t)key * D;
+    float* dvrow =
+        (a.gsplit > 1 ? a.part + (a.gsplit + slice) * kvsize : a.dv) + head + (size_t)key * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -387,14 +392,16 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
 
   const int N = a.N;
   const int nkt = (N + BK - 1) / BK;
-  const int total = nkt * a.B * a.Hkv;
+  const int total = nkt * a.B * a.Hkv * a.gsplit;
   const int w = xcd_remap(blockIdx.x, total);
-  int bkv = w / nkt;
+  int bkv = w / nkt;  // (K/V head) * gsplit + slice
   int kt = w % nkt;
   if constexpr (CAUSAL) causal_order(w, total, nkt, bkv, kt);
+  const int slice = bkv % a.gsplit;
+  bkv /= a.gsplit;
   const int kt0 = kt * BK;
-  const int G = a.H / a.Hkv;
-  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * G;
+  const int G = a.H / a.Hkv / a.gsplit;  // query heads of this slice
+  const int bq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * (a.H / a.Hkv) + slice * G;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -642,13 +649,16 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4*>(row + 32 * b + 8 * g + 4 * h) = v4;
       }
   };
+  const size_t kvsize = (size_t)a.B * a.Hkv * N * D;
+  float* dkout = a.gsplit > 1 ? a.part + slice * kvsize : a.dk;
+  float* dvout = a.gsplit > 1 ? a.part + (a.gsplit + slice) * kvsize : a.dv;
   if (qh == 1) put(dk);
   __syncthreads();
-  if (qh == 0) add_store(dk, a.dk, a.scale);
+  if (qh == 0) add_store(dk, dkout, a.scale);
   __syncthreads();
   if (qh == 0) put(dv);
   __syncthreads();
-  if (qh == 1) add_store(dv, a.dv, 1.f);
+  if (qh == 1) add_store(dv, dvout, 1.f);
 }
 
 // ---------------------------------------------------------------------- dQ
@@ -907,13 +917,28 @@ void bwd_dq_kernel(BwdArgs a) {
 template <int D, int MODE>
 constexpr int kDkdvWaves = 4;
 
+// dK, dV = sum over the query-head slices' partials, in slot order (so the
+// result does not depend on scheduling).  n4: float4 elements per tensor.
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs a, long long n4) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(a.part);
+  f32x4 k4 = p[i], v4 = p[(long long)a.gsplit * n4 + i];
+  for (int sl = 1; sl < a.gsplit; ++sl) {
+    k4 += p[(long long)sl * n4 + i];
+    v4 += p[(long long)(a.gsplit + sl) * n4 + i];
+  }
+  reinterpret_cast<f32x4*>(a.dk)[i] = k4;
+  reinterpret_cast<f32x4*>(a.dv)[i] = v4;
+}
+
 template <int D, int MODE>
 hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
   using TK = DkdvTile<D, kDkdvWaves<D, MODE>>;
   constexpr int BK = D == 128 ? kSplitKeys : TK::BK;  // keys per dK/dV workgroup
   static_assert(!(MODE & kSparse) || 128 % BK == 0, "dK/dV keys must fit one mask tile");
   static_assert(!(MODE & kSparse) || DqTile<D>::BQ == 128, "dQ rows must be one mask tile");
-  const long long g1 = (long long)((a.N + BK - 1) / BK) * a.B * a.Hkv;
+  const long long g1 = (long long)((a.N + BK - 1) / BK) * a.B * a.Hkv * a.gsplit;
   const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (D == 128) {
@@ -921,6 +946,12 @@ hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D, MODE>, MODE>), dim3((unsigned)g1),
                        dim3(TK::THREADS), 0, s, a);
+  }
+  if (a.gsplit > 1) {
+    const long long n4 = (long long)a.B * a.Hkv * a.N * D / 4;
+    const long long g3 = (n4 + 255) / 256;
+    if (g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_dkv_reduce_kernel, dim3((unsigned)g3), dim3(256), 0, s, a, n4);
   }
   hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
   return hipGetLastError();

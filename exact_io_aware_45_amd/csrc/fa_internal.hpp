@@ -43,6 +43,13 @@ struct BwdArgs {
   int mask_block;
   int Hkv;  // K, V, dK, dV are [B][Hkv][N][d]; dK/dV sum over the H/Hkv query heads
   float* lse2;  // workspace: LSE_i * log2(e), [B][H][N] fp32 (written with D)
+  // Grouped heads: each group's query heads are split into gsplit slices of
+  // H / Hkv / gsplit heads, one dK/dV workgroup per slice; with gsplit > 1
+  // the slices write fp32 partial dK (slots 0 .. gsplit-1) and dV (slots
+  // gsplit .. 2 gsplit-1), each [B][Hkv][N][d], to `part`, and a reduction
+  // sums them in slot order.
+  int gsplit;
+  float* part;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

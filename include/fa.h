@@ -151,13 +151,27 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
  * Backward of fa_forward_gqa.  dq is fp32 [B][H][N][d]; dk and dv are fp32
  * [B][Hkv][N][d]: the gradient of a shared K/V head is the sum, over the
  * H / Hkv query heads that read it, of each head's gradient.  The sum is
- * taken inside one workgroup in a fixed order (no atomics): deterministic.
- * workspace: fa_backward_workspace_size(B, H, N, d) bytes (H = query heads).
+ * taken in a fixed order (no atomics): deterministic.
+ * workspace: at least fa_backward_workspace_size(B, H, N, d) bytes
+ * (H = query heads).  With fa_backward_gqa_workspace_size(B, H, Hkv, N, d)
+ * bytes or more, each group's query heads are split over several dK/dV
+ * workgroups whose fp32 partial sums are added in a fixed order afterwards
+ * (needed to fill the chip when B * Hkv is small, e.g. MQA); with less, one
+ * workgroup sums the whole group (same result up to rounding order).
  */
 int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, float* dq, float* dk, float* dv, void* workspace,
                     size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
                     int causal, void* stream);
+
+/*
+ * Workspace bytes with which fa_backward_gqa splits each group's query heads
+ * over several dK/dV workgroups: fa_backward_workspace_size(B, H, N, d) plus
+ * room for the partial sums (2 * S * B * Hkv * N * d fp32, S = the number of
+ * slices, a divisor of H / Hkv).  Equal to fa_backward_workspace_size when no
+ * split is needed; 0 for invalid shapes or groupings.
+ */
+size_t fa_backward_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
 
 /*
  * Forward pass with fp8 inputs: q, k, v hold OCP e4m3 codes (1 sign, 4

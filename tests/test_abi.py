@@ -183,3 +183,24 @@ def test_fp8_argument_errors():
     assert f8(q=MIS) == INV
     assert f8(d=96) == _lib.FA_ERR_UNSUPPORTED
     assert f8(q=None, N=0) == _lib.FA_OK
+
+
+def test_gqa_workspace_size():
+    """Extra room for the sliced dK/dV partials exactly when a group must be
+    split: slices S = the smallest divisor of H/Hkv giving 512 dK/dV
+    workgroups (128 keys each), else H/Hkv."""
+    base = _lib.backward_workspace_size
+    gqa = _lib.backward_gqa_workspace_size
+    # MQA at B1 H32 N8192: 64 key tiles, S = 8 (64 * 8 = 512)
+    assert gqa(1, 32, 1, 8192, 128) == base(1, 32, 8192, 128) + 256 + 2 * 8 * 8192 * 128 * 4
+    # B1 H32 Hkv8: 64 * 8 = 512 workgroups already, no split
+    assert gqa(1, 32, 8, 8192, 128) == base(1, 32, 8192, 128)
+    # Hkv == H: never split
+    assert gqa(4, 16, 16, 4096, 128) == base(4, 16, 4096, 128)
+    # tiny: every divisor is too small, so S = H/Hkv = 4
+    assert gqa(2, 4, 1, 200, 64) == base(2, 4, 200, 64) + 256 + 2 * 4 * 2 * 200 * 64 * 4
+    # invalid grouping or shape
+    assert gqa(1, 6, 4, 128, 64) == 0
+    assert gqa(1, 4, 0, 128, 64) == 0
+    assert gqa(1, 4, 2, 128, 80) == 0
+    assert gqa(1, 4, 2, 0, 64) == 0

@@ -402,6 +402,36 @@ def gqa_parity(B, H, Hkv, N, d, causal, seed, backward=True):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_sliced_and_whole_groups(d, causal):
+    """fa_backward_gqa with the larger workspace splits each group's query
+    heads over several dK/dV workgroups and adds their partials in order;
+    with the plain workspace one workgroup sums the group.  Both match the
+    oracle, and each other up to fp32 summation order."""
+    need_gpu()
+    B, H, Hkv, N = 1, 8, 1, 333
+    log(f"gqa sliced vs whole B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    q, _, _, do = inputs.qkv(B, H, N, d, torch.bfloat16, seed=77, with_dout=True)
+    _, k, v = inputs.qkv(B, Hkv, N, d, torch.bfloat16, seed=78)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = _lib.forward_gqa(qd, kd, vd, causal=causal)
+    small = _lib.backward_workspace_size(B, H, N, d)
+    big = _lib.backward_gqa_workspace_size(B, H, Hkv, N, d)
+    assert big > small
+    whole = _lib.backward_gqa(qd, kd, vd, o, dod, lse, causal=causal,
+                              workspace=torch.empty(small, dtype=torch.uint8, device=DEV))
+    sliced = _lib.backward_gqa(qd, kd, vd, o, dod, lse, causal=causal,
+                               workspace=torch.full((big,), 255, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _, _ = oracle.backward_gqa(q, k, v, do, d ** -0.5, causal)
+    for name, gw, gs, r in zip(("dQ", "dK", "dV"), whole, sliced, (rdq, rdk, rdv)):
+        check(name + " whole", to64(gw.cpu()), r)
+        check(name + " sliced", to64(gs.cpu()), r)
+        assert torch.allclose(gw, gs, rtol=1e-5, atol=1e-5), name
+    assert torch.equal(whole[0], sliced[0])  # dQ does not depend on the split
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("H,Hkv,N", [(4, 2, 65), (4, 1, 200), (6, 3, 333)])
 def test_gqa_small(H, Hkv, N, d, causal):
     need_gpu()
