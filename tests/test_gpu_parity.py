@@ -337,6 +337,32 @@ def backward_parity_sparse(q, k, v, do, causal, pairs, mask):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_mask_rows_longer_than_one_chunk(d, causal):
+    """Mask rows and columns of 71 blocks (N = 9000); the kernels read the mask
+    64 entries at a time.  Rows 0-9 see only block 70 (in the second chunk;
+    causal: nothing), rows 10-19 see nothing (O = 0, LSE = -inf, dQ = 0), the
+    rest see the diagonal and blocks 3 and 66; no row sees block 5 (dK = dV =
+    0 there)."""
+    need_gpu()
+    N, nb = 9000, 71
+    log(f"block-sparse 71-block mask rows B1 H2 N{N} d{d} causal={causal}")
+    mask = torch.zeros(nb, nb, dtype=torch.uint8)
+    mask[0:10, 70] = 1
+    for i in range(20, nb):
+        mask[i, i] = 1
+        mask[i, 3] = 1
+        mask[i, 66] = 1
+    q, k, v, do = inputs.qkv(1, 2, N, d, torch.bfloat16, seed=900 + d, with_dout=True)
+    o, lse = forward_parity(q, k, v, causal, all_pairs(q), mask=mask)
+    dead = slice(0, 1280) if causal else slice(1280, 2560)
+    assert torch.all(o[:, :, dead] == 0) and torch.all(torch.isneginf(lse[:, :, dead]))
+    dq, dk, dv = backward_parity_sparse(q, k, v, do, causal, all_pairs(q), mask)
+    assert torch.all(dq[:, :, dead] == 0)
+    assert torch.all(dk[:, :, 640:768] == 0) and torch.all(dv[:, :, 640:768] == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [100, 300, 700])
 def test_blocksparse_backward_small(N, d, causal):
     need_gpu()
@@ -432,6 +458,23 @@ def test_gqa_backward_sliced_and_whole_groups(d, causal):
         check(name + " sliced", to64(gs.cpu()), r, scale=grow)
         assert torch.allclose(gw, gs, rtol=1e-5, atol=1e-5), name
     assert torch.equal(whole[0], sliced[0])  # dQ does not depend on the split
+
+
+def test_gqa_sliced_backward_is_deterministic():
+    """The sliced grouped-head backward adds the slices' partials in a fixed
+    order: two runs give bitwise the same gradients."""
+    need_gpu()
+    B, H, Hkv, N, d = 1, 8, 1, 700, 128
+    q, _, _, do = (t.to(DEV) for t in inputs.qkv(B, H, N, d, torch.bfloat16, seed=3,
+                                                  with_dout=True))
+    _, k, v = (t.to(DEV) for t in inputs.qkv(B, Hkv, N, d, torch.bfloat16, seed=4))
+    o, lse = _lib.forward_gqa(q, k, v, causal=True)
+    assert _lib.backward_gqa_workspace_size(B, H, Hkv, N, d) > _lib.backward_workspace_size(B, H, N, d)
+    a = _lib.backward_gqa(q, k, v, o, do, lse, causal=True)
+    b = _lib.backward_gqa(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 def test_mqa_backward_sliced_long():
