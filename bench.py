@@ -16,19 +16,25 @@ on.  Prints ONE JSON line:
                same treatment in roofline_bwd
   cpu_baseline the fp64 CPU oracle, timed on this host on a bounded sample of
                the same workload (whole heads, the same passes)
+  sclk_mhz     the sustained shader clock the driver reports, sampled over
+               the second half of --clock-window seconds of untimed steps run
+               after the timed ones (its reading trails the load)
 
 --workload runs one of the other named workloads (exact_io_aware_45_amd.inputs)
 with the same line format; forward-only workloads time fa_forward alone.
 --fp8 runs a dense workload's forward through fa_forward_fp8 (e4m3 inputs),
 priced against the fp8 peak.  --cold writes a 512 MiB buffer before every step
 (untimed), so that the inputs come from HBM rather than the last-level cache.
+--kv-heads HKV runs a dense workload through the grouped-head entry points.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +110,72 @@ def load_traffic(path: str) -> dict:
     shas = t.get("source_sha", {})
     return {k: t[k] for k, files in KERNEL_SOURCES.items()
             if k in t and shas.get(k) == source_sha(files)}
+
+
+class ClockSampler:
+    """Samples the shader clock the driver reports (the line marked '*' of
+    pp_dpm_sclk) every `period` seconds on a background thread; summary() is
+    None where the file is not readable.  The driver's value trails the load
+    by a few hundred milliseconds (it reads ~850 MHz over a 50 ms burst that
+    sustains ~1.95 GHz), so summary(after=t) keeps the samples from time t on."""
+
+    def __init__(self, period: float = 0.002):
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if len(paths) == 1 else None  # one GPU: one card
+        self.period, self.mhz, self.at = period, [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().rstrip("*").strip().lower()
+                               .replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except (OSError, ValueError, IndexError):
+                return
+            if v is not None:
+                self.mhz.append(v)
+                self.at.append(time.perf_counter())
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self, after: float = 0.0, source: str = ""):
+        mhz = [m for m, t in zip(self.mhz, self.at) if t >= after]
+        if not mhz:
+            return None
+        return {"mean": round(sum(mhz) / len(mhz), 1), "min": min(mhz), "max": max(mhz),
+                "samples": len(mhz), "source": source or "pp_dpm_sclk"}
+
+
+def sustained_clock(step, seconds: float):
+    """Runs `step` back to back (untimed) for `seconds` and returns the shader
+    clock the driver reports over the second half of that window."""
+    import torch
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+    return clock.summary(after=t0 + seconds / 2,
+                         source=f"pp_dpm_sclk every 2 ms over the second half of {seconds:g} s "
+                                "of untimed steps run after the timed ones")
 
 
 def cpu_baseline(w, inp, passes, mask=None, budget_s: float = 15.0, max_heads: int = 32):
@@ -212,6 +284,9 @@ def main():
                          "the inputs are not served from the 256 MB last-level cache")
     ap.add_argument("--fp8", action="store_true",
                     help="fp8 (OCP e4m3) inputs through fa_forward_fp8, forward only")
+    ap.add_argument("--clock-window", type=float, default=0.6,
+                    help="seconds of untimed steps after the timed ones, over which the "
+                         "sustained shader clock is sampled (0: skip)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped K/V heads: run a dense bf16 workload through fa_forward_gqa "
                          "(and fa_backward_gqa) with this many K/V heads")
@@ -346,6 +421,7 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = sustained_clock(step, args.clock_window) if args.clock_window > 0 else None
     total_ms = start.elapsed_time(end)
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -416,6 +492,7 @@ def main():
     line["device"] = {"name": props.name, "cus": props.multi_processor_count,
                       "hip_runtime": _lib.runtime_version(), "libfa": _lib.version()}
     line["wall_s_timed_region"] = round(wall, 3)
+    line["sclk_mhz"] = sclk
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, passes, mask)
     print(json.dumps(line), flush=True)

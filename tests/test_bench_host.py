@@ -70,3 +70,22 @@ def test_grouped_head_traffic():
     assert bench.traffic_bytes(g, "bwd") == 3 * t + 2 * kv + rows + 2 * t + 4 * kv + 2 * rows
     assert bench.traffic_bytes(w, "bwd") == 5 * t + rows + 6 * t + 2 * rows
     assert bench.flops(g, "fwd") == bench.flops(w, "fwd")
+
+
+def test_clock_sampler_reads_the_marked_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1893Mhz *\n2: 2400Mhz\n")
+    c = bench.ClockSampler(period=0.001)
+    c.path = str(f)
+    assert c._read() == 1893
+    with c:
+        import time
+        time.sleep(0.01)
+    s = c.summary()
+    assert s["mean"] == 1893 and s["min"] == 1893 and s["samples"] >= 1
+    assert c.summary(after=time.perf_counter() + 10) is None
+    none = bench.ClockSampler()
+    none.path = None
+    with none:
+        pass
+    assert none.summary() is None
