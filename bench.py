@@ -9,7 +9,8 @@ on.  Prints ONE JSON line:
   value        whole-step TFLOP/s with the algorithmic FLOP counts
                forward 4*B*H*N^2*d, backward 10*B*H*N^2*d, both halved for causal
                (block-sparse: 4*d resp. 10*d per visible (query, key) pair)
-  fwd / bwd    each pass's own time, TFLOP/s and fraction of the bf16 MFMA peak
+  fwd / bwd    each pass's own time (mean, median and minimum over the timed
+               steps), TFLOP/s and fraction of the bf16 MFMA peak
   roofline     the forward kernel (one launch per fa_forward) against the bf16
                dense MFMA peak, or against HBM bandwidth when its arithmetic
                intensity is below the ridge point; the backward call gets the
@@ -423,8 +424,15 @@ def main():
     wall = time.perf_counter() - t0
     sclk = sustained_clock(step, args.clock_window) if args.clock_window > 0 else None
     total_ms = start.elapsed_time(end)
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    fwd_each = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    bwd_each = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    fwd_ms = sum(fwd_each) / args.steps
+    bwd_ms = sum(bwd_each) / args.steps
+
+    def spread(each):  # median and minimum of the per-step event times
+        n = len(each)
+        med = each[n // 2] if n % 2 else 0.5 * (each[n // 2 - 1] + each[n // 2])
+        return {"ms_median": round(med, 4), "ms_min": round(each[0], 4)}
     # cold runs: the step is the passes alone (the flush between them is not timed)
     ms_per_step = (fwd_ms + bwd_ms) if args.cold else total_ms / args.steps
 
@@ -469,7 +477,7 @@ def main():
                    "cache": "cold" if args.cold else "warm",
                    "seed": args.seed},
         "frac_of_peak": round(value / peak, 4),
-        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tf, 2),
+        "fwd": {"ms": round(fwd_ms, 4), **spread(fwd_each), "tflops": round(fwd_tf, 2),
                 "frac_of_peak": round(fwd_tf / peak, 4), "flops": ff},
         "roofline": roofline(w, "fwd", fwd_ms, ff, traffic.get("fwd_bf16_kernel"), fwd_kernel),
     }
@@ -483,7 +491,7 @@ def main():
             flops(dataclasses.replace(w, sparse=False), "fwd") / (fwd_ms * 1e-3) / 1e12, 2)
     if "bwd" in passes:
         bwd_tf = fb / (bwd_ms * 1e-3) / 1e12
-        line["bwd"] = {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 2),
+        line["bwd"] = {"ms": round(bwd_ms, 4), **spread(bwd_each), "tflops": round(bwd_tf, 2),
                        "frac_of_peak": round(bwd_tf / peak, 4), "flops": fb}
         line["roofline_bwd"] = roofline(
             w, "bwd", bwd_ms, fb, traffic.get("fa_backward"),
