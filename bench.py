@@ -156,6 +156,18 @@ class ClockSampler:
             self._stop.set()
             self._thread.join()
 
+    def max_mhz(self):
+        """The highest clock level the driver lists (the device's peak clock)."""
+        if not self.path:
+            return None
+        try:
+            with open(self.path) as f:
+                levels = [int(line.split(":")[1].strip().rstrip("*").strip().lower()
+                              .replace("mhz", "")) for line in f if ":" in line]
+        except (OSError, ValueError, IndexError):
+            return None
+        return max(levels) if levels else None
+
     def summary(self, after: float = 0.0, source: str = ""):
         mhz = [m for m, t in zip(self.mhz, self.at) if t >= after]
         if not mhz:
@@ -499,6 +511,11 @@ def main():
             "bwd_dq launches")
     line["device"] = {"name": props.name, "cus": props.multi_processor_count,
                       "hip_runtime": _lib.runtime_version(), "libfa": _lib.version()}
+    max_mhz = ClockSampler().max_mhz()
+    if max_mhz:  # bf16 dense peak from the device: CUs x peak clock x 4096 FLOP/clk/CU
+        line["device"]["max_sclk_mhz"] = max_mhz
+        line["device"]["bf16_peak_tflops"] = round(
+            props.multi_processor_count * max_mhz * 1e6 * 4096 / 1e12, 1)
     line["wall_s_timed_region"] = round(wall, 3)
     line["sclk_mhz"] = sclk
     if not args.no_cpu_baseline:

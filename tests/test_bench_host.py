@@ -84,6 +84,9 @@ def test_clock_sampler_reads_the_marked_level(tmp_path):
     s = c.summary()
     assert s["mean"] == 1893 and s["min"] == 1893 and s["samples"] >= 1
     assert c.summary(after=time.perf_counter() + 10) is None
+    assert c.max_mhz() == 2400
+    # 256 CUs at the listed 2400 MHz give the peak the roofline uses
+    assert abs(256 * c.max_mhz() * 1e6 * 4096 / 1e12 - bench.PEAK_BF16_TFLOPS) < 0.1
     none = bench.ClockSampler()
     none.path = None
     with none:
