@@ -212,8 +212,16 @@ def cpu_baseline(w, inp, passes, mask=None, budget_s: float = 15.0, max_heads: i
         done += 1
     per_head = sum(flops(w, p, mask) for p in passes) / (w.B * w.H)
     what = " + ".join({"fwd": "forward", "bwd": "backward"}[p] for p in passes)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         None)
+    except OSError:
+        pass
     return {"value": round(per_head * done / t_total / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)), "cpu_model": model, "kind": "oracle",
             "sample": f"{done} whole head(s) of the workload ({what}, all {w.N} rows), "
                       f"{t_total:.1f} s, fp64, same FLOP convention"}
 
