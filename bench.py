@@ -248,39 +248,6 @@ def roofline(w, which, ms, fl, traffic, kernel):
     return r
 
 
-CEILING_SRC = os.path.join(ROOT, "bench_mfma_ceiling.hip")
-CEILING_BIN = os.path.join(ROOT, "_build", "bench_mfma_ceiling")
-
-
-def build_mfma_ceiling() -> str:
-    """Compile bench_mfma_ceiling.hip for gfx950 (hipcc)."""
-    import subprocess
-    from exact_io_aware_45_amd import build as fa_build
-    os.makedirs(os.path.dirname(CEILING_BIN), exist_ok=True)
-    cmd = [fa_build.hipcc(), "--offload-arch=gfx950", "-O3", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument", CEILING_SRC,
-           "-o", CEILING_BIN]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return CEILING_BIN
-
-
-def mfma_ceiling() -> None:
-    """Sustained bf16 MFMA rate of one attention tile's matrix work, zeros vs random data."""
-    import subprocess
-    if not os.path.exists(CEILING_BIN):
-        build_mfma_ceiling()
-    r = subprocess.run([CEILING_BIN], capture_output=True, text=True, timeout=120)
-    if r.returncode != 0:
-        print(r.stdout + r.stderr)
-        sys.exit(r.returncode)
-    rows = [json.loads(x) for x in r.stdout.splitlines() if x.startswith("{")]
-    best = {d: max(x["tflops"] for x in rows if x["data"] == d) for d in ("zeros", "random")}
-    print(json.dumps({"metric": "sustained bf16 MFMA rate, attention-tile instruction mix",
-                      "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "runs": rows,
-                      "best_zeros": best["zeros"], "best_random": best["random"],
-                      "best_random_frac": round(best["random"] / PEAK_BF16_TFLOPS, 4)}))
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,8 +259,6 @@ def main():
                     help="first run one device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters, if present")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="measure the sustained bf16 MFMA rate (bench_mfma_ceiling.hip) and exit")
     ap.add_argument("--workload", default="long_d128_causal",
                     help="named workload (exact_io_aware_45_amd.inputs.WORKLOADS)")
     ap.add_argument("--causal", choices=("default", "on", "off"), default="default",
@@ -313,9 +278,6 @@ def main():
                          "(and fa_backward_gqa) with this many K/V heads")
     args = ap.parse_args()
 
-    if args.mfma_ceiling:
-        mfma_ceiling()
-        return
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))

@@ -10,7 +10,8 @@
  * pages state that the tiled method reaches the same result as standard
  * attention up to floating-point rounding ("FlashAttention." plate, section
  * "Never write the scores"; "FlashAttention: Fast and Memory-Efficient Exact
- * Attention with IO-Awareness", DarcStar commentary: "same answer, exactly").
+ * Attention with IO-Awareness", DarcStar commentary, which says the tiled
+ * result equals the standard one).
  * Standard attention is spelled out in the opening of the "FlashAttention."
  * plate: S = Q K^T, a row softmax of S, then P V.  Every step below follows
  * that order, one query row at a time, in double precision, with libm's

@@ -3,8 +3,10 @@ element by element, on seeded synthetic inputs.
 
 Small cases span several tiles and a ragged tail and are compared in full.
 The five full-size workloads run in the same launch configuration the
-benchmark times; their outputs are compared on sampled (batch, head) pairs,
-which the oracle computes completely (heads are independent).
+benchmark times, and every element of every (batch, head) is compared with
+the oracle, which streams the heads in chunks (heads are independent).  Their
+outputs are written into buffers pre-filled with NaN, so an element the
+kernels never write fails the comparison.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import torch
 
 import oracle
 from exact_io_aware_45_amd import _lib, inputs
-from _parity import check, check_lse, log, to64
+from _parity import Stats, check, check_lse, log, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +46,83 @@ def all_pairs(t):
     return [(b, h) for b in range(t.shape[0]) for h in range(t.shape[1])]
 
 
-def sample_pairs(B, H, n, seed=0):
-    rng = np.random.default_rng(seed)
-    flat = rng.choice(B * H, size=min(n, B * H), replace=False)
-    return [(int(i) // H, int(i) % H) for i in sorted(flat)]
+def chunks(pairs, n):
+    for i in range(0, len(pairs), n):
+        yield pairs[i:i + n]
+
+
+NAN = float("nan")
+
+
+def nan_fwd_out(q, odtype=None):
+    """(o, lse) device buffers pre-filled with NaN."""
+    B, H, N, _ = q.shape
+    return (torch.full(q.shape, NAN, dtype=odtype or q.dtype, device=DEV),
+            torch.full((B, H, N), NAN, dtype=torch.float32, device=DEV))
+
+
+def nan_bwd_out(q, k):
+    """(dq, dk, dv) fp32 device buffers pre-filled with NaN."""
+    return (torch.full(q.shape, NAN, dtype=torch.float32, device=DEV),
+            torch.full(k.shape, NAN, dtype=torch.float32, device=DEV),
+            torch.full(k.shape, NAN, dtype=torch.float32, device=DEV))
+
+
+def forward_parity_all_heads(q, k, v, causal, mask=None, chunk=8):
+    """The whole forward output (every head, row and column) against the
+    oracle, written over NaN-filled buffers."""
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = nan_fwd_out(qd)
+    if mask is None:
+        o, lse = _lib.forward(qd, kd, vd, causal=causal, out=out)
+    else:
+        o, lse = _lib.forward_blocksparse(qd, kd, vd, mask.to(DEV), causal=causal, out=out)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any(), "unwritten output"
+    scale = q.shape[-1] ** -0.5
+    so, sl = Stats("O"), Stats("lse")
+    for pc in chunks(all_pairs(q), chunk):
+        ro, rl = oracle.forward(heads_of(q, pc), heads_of(k, pc), heads_of(v, pc), scale, causal,
+                                block_mask=None if mask is None else mask.numpy(),
+                                mask_block=128)
+        so.add(heads_of(o, pc), ro)
+        check_lse(torch.stack([lse[b, h] for b, h in pc]), rl, stats=sl)
+    so.check()
+    sl.check()
+    return o, lse
+
+
+def backward_parity_all_heads(q, k, v, do, causal, mask=None, chunk=8):
+    """Forward (LSE) and the whole backward output against the oracle, the
+    gradients written over NaN-filled buffers."""
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out = nan_bwd_out(qd, kd)
+    if mask is None:
+        o, lse = _lib.forward(qd, kd, vd, causal=causal)
+        dq, dk, dv = _lib.backward(qd, kd, vd, o, dod, lse, causal=causal, out=out)
+    else:
+        md = mask.to(DEV)
+        o, lse = _lib.forward_blocksparse(qd, kd, vd, md, causal=causal)
+        dq, dk, dv = _lib.backward_blocksparse(qd, kd, vd, o, dod, lse, md, causal=causal,
+                                               out=out)
+    torch.cuda.synchronize()
+    dq, dk, dv, lse = dq.cpu(), dk.cpu(), dv.cpu(), lse.cpu()
+    for name, g in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert not torch.isnan(g).any(), f"unwritten {name}"
+    scale = q.shape[-1] ** -0.5
+    st = {n: Stats(n) for n in ("dQ", "dK", "dV", "lse")}
+    for pc in chunks(all_pairs(q), chunk):
+        rdq, rdk, rdv, rl, _ = oracle.backward(heads_of(q, pc), heads_of(k, pc),
+                                               heads_of(v, pc), heads_of(do, pc), scale, causal,
+                                               block_mask=None if mask is None else mask.numpy(),
+                                               mask_block=128)
+        for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+            st[name].add(heads_of(g, pc), r)
+        check_lse(torch.stack([lse[b, h] for b, h in pc]), rl, stats=st["lse"])
+    for x in st.values():
+        x.check()
+    return dq, dk, dv
 
 
 def forward_parity(q, k, v, causal, pairs, mask=None, bf16=True):
@@ -93,14 +168,16 @@ def test_forward_f32_single_head_workload():
         forward_parity(x["q"], x["k"], x["v"], w.causal, all_pairs(x["q"]), bf16=False)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["batched_d64", "batched_d64_causal", "long_d128_causal"])
-def test_forward_full_workloads(name):
+def test_forward_full_workloads(name, seed):
+    """Every head of the batched (B8 H16 N1024 d64, causal and not) and long
+    (B1 H32 N8192 d128 causal) forward workloads."""
     need_gpu()
     w = inputs.WORKLOADS[name]
-    for seed in (0, 1, 2):
-        log(f"{name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal})")
-        x = inputs.workload_inputs(w, seed)
-        forward_parity(x["q"], x["k"], x["v"], w.causal, sample_pairs(w.B, w.H, 4, seed))
+    log(f"{name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal}), all heads")
+    x = inputs.workload_inputs(w, seed)
+    forward_parity_all_heads(x["q"], x["k"], x["v"], w.causal)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -112,7 +189,7 @@ def test_forward_eight_wave_grid(N, causal):
     need_gpu()
     log(f"forward bf16 B4 H130 N{N} d128 causal={causal} (8-wave grid)")
     q, k, v = inputs.qkv(4, 130, N, 128, torch.bfloat16, seed=1000 + N)
-    forward_parity(q, k, v, causal, sample_pairs(4, 130, 6, seed=N))
+    forward_parity_all_heads(q, k, v, causal, chunk=130)
 
 
 def test_caller_outputs_match_fresh_outputs():
@@ -225,23 +302,23 @@ def test_backward_small(N, d, causal):
     backward_parity(q, k, v, do, causal, all_pairs(q))
 
 
-def test_backward_full_workload():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_backward_full_workload(seed):
+    """Every head of the backward workload (B4 H16 N4096 d128 causal)."""
     need_gpu()
     w = inputs.WORKLOADS["bwd_d128_causal"]
-    for seed in (0, 1, 2):
-        log(f"{w.name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal})")
-        x = inputs.workload_inputs(w, seed)
-        backward_parity(x["q"], x["k"], x["v"], x["dout"], w.causal,
-                        sample_pairs(w.B, w.H, 4, seed))
+    log(f"{w.name} seed {seed} (B{w.B} H{w.H} N{w.N} d{w.d} causal={w.causal}), all heads")
+    x = inputs.workload_inputs(w, seed)
+    backward_parity_all_heads(x["q"], x["k"], x["v"], x["dout"], w.causal)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_batched_d64(causal):
-    """d=64 backward at the batched shape (B8 H16 N1024), sampled heads."""
+    """d=64 backward at the batched shape (B8 H16 N1024), every head."""
     need_gpu()
-    log(f"backward B8 H16 N1024 d64 causal={causal}")
+    log(f"backward B8 H16 N1024 d64 causal={causal}, all heads")
     q, k, v, do = inputs.qkv(8, 16, 1024, 64, torch.bfloat16, seed=5, with_dout=True)
-    backward_parity(q, k, v, do, causal, sample_pairs(8, 16, 6, 5))
+    backward_parity_all_heads(q, k, v, do, causal, chunk=32)
 
 
 def test_backward_is_deterministic():
@@ -274,16 +351,17 @@ def test_blocksparse_small(N, d, causal):
     forward_parity(q, k, v, causal, all_pairs(q), mask=mask)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("causal", [False, True])
-def test_blocksparse_full_workload(causal):
+def test_blocksparse_full_workload(causal, seed):
+    """Every head of the block-sparse workload (B1 H16 N16384 d64, 2048 of
+    16384 tiles)."""
     need_gpu()
     w = inputs.WORKLOADS["blocksparse_d64"]
-    for seed in ((0, 1, 2) if not causal else (0,)):
-        x = inputs.workload_inputs(w, seed)
-        log(f"{w.name} seed {seed} causal={causal}: {int(x['mask'].sum())} of "
-            f"{x['mask'].numel()} tiles")
-        forward_parity(x["q"], x["k"], x["v"], causal, sample_pairs(w.B, w.H, 4, seed),
-                       mask=x["mask"])
+    x = inputs.workload_inputs(w, seed)
+    log(f"{w.name} seed {seed} causal={causal}: {int(x['mask'].sum())} of "
+        f"{x['mask'].numel()} tiles, all heads")
+    forward_parity_all_heads(x["q"], x["k"], x["v"], causal, mask=x["mask"])
 
 
 def test_blocksparse_mask_identities():
@@ -380,15 +458,17 @@ def test_blocksparse_backward_small(N, d, causal):
         assert torch.all(dk[:, :, 256:384] == 0) and torch.all(dv[:, :, 256:384] == 0)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("causal", [False, True])
-def test_blocksparse_backward_full_workload(causal):
+def test_blocksparse_backward_full_workload(causal, seed):
+    """Every head of the block-sparse workload's backward (dO drawn fourth
+    from the same seed, as for the dense backward workload)."""
     need_gpu()
     w = inputs.WORKLOADS["blocksparse_d64"]
-    x = inputs.workload_inputs(w, 0)
-    do = inputs.qkv(w.B, w.H, w.N, w.d, torch.bfloat16, seed=0, with_dout=True)[3]
-    log(f"{w.name} backward causal={causal}")
-    backward_parity_sparse(x["q"], x["k"], x["v"], do, causal, sample_pairs(w.B, w.H, 2, 3),
-                           x["mask"])
+    q, k, v, do = inputs.qkv(w.B, w.H, w.N, w.d, torch.bfloat16, seed=seed, with_dout=True)
+    mask = inputs.block_mask(w.N, w.mask_block, w.band, w.density, seed)
+    log(f"{w.name} backward seed {seed} causal={causal}, all heads")
+    backward_parity_all_heads(q, k, v, do, causal, mask=mask)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -424,9 +504,10 @@ def gqa_parity(B, H, Hkv, N, d, causal, seed, backward=True):
         rdq, rdk, rdv, _, _ = oracle.backward_gqa(q, k, v, do, scale, causal)
         check("dQ", to64(dq.cpu()), rdq)
         # A shared head's dK, dV sum H/Hkv per-head gradients with independent
-        # rounding errors: the bounds grow as sqrt(H/Hkv).
+        # rounding errors: the max bound grows as sqrt(H/Hkv).  The mean bound
+        # is not widened.
         for name, g, r in (("dK", dk, rdk), ("dV", dv, rdv)):
-            check(name, to64(g.cpu()), r, scale=(H // Hkv) ** 0.5)
+            check(name, to64(g.cpu()), r, max_scale=(H // Hkv) ** 0.5)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -454,8 +535,8 @@ def test_gqa_backward_sliced_and_whole_groups(d, causal):
     rdq, rdk, rdv, _, _ = oracle.backward_gqa(q, k, v, do, d ** -0.5, causal)
     for name, gw, gs, r in zip(("dQ", "dK", "dV"), whole, sliced, (rdq, rdk, rdv)):
         grow = 1.0 if name == "dQ" else (H // Hkv) ** 0.5  # sum over the group
-        check(name + " whole", to64(gw.cpu()), r, scale=grow)
-        check(name + " sliced", to64(gs.cpu()), r, scale=grow)
+        check(name + " whole", to64(gw.cpu()), r, max_scale=grow)
+        check(name + " sliced", to64(gs.cpu()), r, max_scale=grow)
         assert torch.allclose(gw, gs, rtol=1e-5, atol=1e-5), name
     assert torch.equal(whole[0], sliced[0])  # dQ does not depend on the split
 
@@ -525,7 +606,8 @@ def test_gqa_with_hkv_equal_h_is_plain_attention():
 # stored as w' = 2^8 exp(s - m), rounded with relative error <= 2^-4 in the
 # normal range and absolute error <= 2^-10 below it, and the row sum uses the
 # unrounded weights.  So, per output element,
-#   |dO_c| <= sum_j (2^-4 w_j + 2^-10 / L') |v_jc| + fp32 accumulation + bf16 output,
+#   |dO_c| <= sum_j (2^-4 w_j + 2^-10 / L') |v_jc| + fp32 accumulation
+#             + 2^-8 |O_c| (bf16 output rounding),
 # with w_j = exp(s_j - LSE) the oracle's weights and L' = 2^8 sum_j exp(s_j - m) >= 2^8.
 # (The bf16 tolerance of the other tests does not apply: e4m3 keeps 3 mantissa
 # bits, so a row with few visible keys can legitimately miss by more.)
@@ -551,29 +633,41 @@ def fp8_bound(qd, kd, vd, lse, scale, causal):
     return out
 
 
-def fp8_parity(B, H, N, d, causal, seed, pairs=None):
+def fp8_parity(B, H, N, d, causal, seed, chunk=8):
+    """Every head of an fp8 forward against the oracle on the dequantized
+    inputs, each element within its derived bound (output over NaN)."""
     (q8, qs), (k8, ks), (v8, vs) = inputs.qkv_fp8(B, H, N, d, seed=seed)
-    o, lse = _lib.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), qs, ks, vs, causal=causal)
+    out = nan_fwd_out(q8, odtype=torch.bfloat16)
+    o, lse = _lib.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), qs, ks, vs, causal=causal,
+                              out=out)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
-    pairs = pairs or all_pairs(q8)
-    qd, kd, vd = (fp8_dequant(c, s, pairs) for c, s in ((q8, qs), (k8, ks), (v8, vs)))
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any(), "unwritten output"
     scale = d ** -0.5
-    ro, rl = oracle.forward(qd, kd, vd, scale, causal)
-    go = np.stack([to64(o[b, h]) for b, h in pairs])
-    gl = np.stack([to64(lse[b, h]) for b, h in pairs])
-    err = np.abs(go - ro)
-    bound = fp8_bound(qd, kd, vd, rl, scale, causal) + 2.0 ** -9 * np.abs(ro) + 1e-6
-    log(f"  fp8 O: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
-        f"max err/bound={float((err / bound).max()):.3f}")
-    assert bool((err <= bound).all()), "fp8 O outside its derived error bound"
+    worst, esum, bsum, n, lmax, emax = 0.0, 0.0, 0.0, 0, 0.0, 0.0
+    for pairs in chunks(all_pairs(q8), chunk):
+        qd, kd, vd = (fp8_dequant(c, s, pairs) for c, s in ((q8, qs), (k8, ks), (v8, vs)))
+        ro, rl = oracle.forward(qd, kd, vd, scale, causal)
+        go = np.stack([to64(o[b, h]) for b, h in pairs])
+        gl = np.stack([to64(lse[b, h]) for b, h in pairs])
+        err = np.abs(go - ro)
+        # bf16 output rounding: relative error at most 2^-8 (half an ulp of an
+        # 8-significant-bit format).
+        bound = fp8_bound(qd, kd, vd, rl, scale, causal) + 2.0 ** -8 * np.abs(ro) + 1e-6
+        assert bool((err <= bound).all()), "fp8 O outside its derived error bound"
+        worst = max(worst, float((err / bound).max()))
+        emax = max(emax, float(err.max()))
+        esum += float(err.sum())
+        bsum += float(bound.sum())
+        n += err.size
+        lmax = max(lmax, float(np.abs(gl - rl).max()))
+    log(f"  fp8 O: max_abs={emax:.3e} mean_abs={esum / n:.3e} max err/bound={worst:.3f}")
     # The bound lines every rounding up against the output; independent
     # roundings leave the typical element far inside it.  A systematic error
     # (a wrong scale, a biased rounding) would not.
-    assert err.mean() <= 0.25 * bound.mean(), (err.mean(), bound.mean())
-    lerr = np.abs(gl - rl)
-    log(f"  fp8 LSE: max_abs={lerr.max():.3e}")
-    assert lerr.max() <= 1e-3
+    assert esum <= 0.25 * bsum, (esum / n, bsum / n)
+    log(f"  fp8 LSE: max_abs={lmax:.3e}")
+    assert lmax <= 1e-3
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -586,13 +680,13 @@ def test_fp8_forward_small(N, d, causal):
 
 
 def test_fp8_forward_long_workload():
-    """The long causal shape (B1 H32 N8192 d128) in fp8, two sampled heads."""
+    """The long causal shape (B1 H32 N8192 d128) in fp8, every head."""
     need_gpu()
-    log("fp8 forward B1 H32 N8192 d128 causal")
-    fp8_parity(1, 32, 8192, 128, True, seed=0, pairs=sample_pairs(1, 32, 2, 0))
+    log("fp8 forward B1 H32 N8192 d128 causal, all heads")
+    fp8_parity(1, 32, 8192, 128, True, seed=0, chunk=4)
 
 
 def test_fp8_forward_batched_workload():
     need_gpu()
-    log("fp8 forward B8 H16 N1024 d64 non-causal")
-    fp8_parity(8, 16, 1024, 64, False, seed=1, pairs=sample_pairs(8, 16, 3, 1))
+    log("fp8 forward B8 H16 N1024 d64 non-causal, all heads")
+    fp8_parity(8, 16, 1024, 64, False, seed=1, chunk=32)
