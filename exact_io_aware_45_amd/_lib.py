@@ -16,8 +16,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(_HERE, "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 8 << 20  # FA_NOALLOC_SCRATCH_BYTES
 SYMBOLS = ("fa_forward", "fa_forward_f32", "fa_backward_workspace_size", "fa_backward",
+           "fa_backward_noalloc",
            "fa_forward_blocksparse", "fa_backward_blocksparse", "fa_forward_gqa",
            "fa_backward_gqa", "fa_backward_gqa_workspace_size", "fa_forward_fp8",
            "fa_error_string", "fa_version", "fa_runtime_version")
@@ -51,6 +53,7 @@ def load():
     lib.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_backward_gqa_workspace_size.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
     lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i,
                                             i, f, i, vp, i, vp]
     lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
@@ -58,6 +61,7 @@ def load():
     lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f,
                                     i, vp]
     for name in ("fa_forward", "fa_forward_f32", "fa_forward_blocksparse", "fa_backward",
+                 "fa_backward_noalloc",
                  "fa_backward_blocksparse", "fa_forward_gqa", "fa_backward_gqa",
                  "fa_forward_fp8", "fa_version", "fa_runtime_version"):
         getattr(lib, name).restype = i
@@ -239,6 +243,29 @@ def backward(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
                            _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), B, H, N, d,
                            _scale(scale, d), int(bool(causal)), _stream(q.device)),
            "fa_backward")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+                     out=None):
+    """fa_backward_noalloc: fa_backward with the library's fixed per-device
+    scratch as workspace (B*H*N <= 1048576 rows).  Returns (dq, dk, dv)."""
+    lib = load()
+    B, H, _, N, d = _shape(q, k, v, torch.bfloat16)
+    _tensor("o", o, torch.bfloat16, q.shape)
+    _tensor("dout", dout, torch.bfloat16, q.shape)
+    _tensor("lse", lse, torch.float32, (B, H, N))
+    if out is None:
+        dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device)
+                      for _ in range(3))
+    else:
+        dq, dk, dv = out
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _tensor(name, t, torch.float32, q.shape)
+    _check(lib.fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
+                                   int(bool(causal)), _stream(q.device)),
+           "fa_backward_noalloc")
     return dq, dk, dv
 
 

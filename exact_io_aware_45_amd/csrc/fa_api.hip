@@ -1,15 +1,27 @@
 // fa_api.hip -- the C ABI declared in include/fa.h: argument validation and
-// dispatch to the kernel launchers.  No allocation, no global state.
+// dispatch to the kernel launchers.  No allocation; the only state is the
+// fixed scratch array of fa_backward_noalloc and its per-device address.
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_internal.hpp"
 
+// Scratch of fa_backward_noalloc: the backward workspace (D, then
+// LSE * log2(e), one fp32 each per row) for callers that cannot allocate.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` only names the array: its device address on each
+// GPU comes from hipGetSymbolAddress, taken once per device with that device
+// current (scratch_address below), and only that address is passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -117,6 +129,28 @@ int backward_common(const void* q, const void* k, const void* v, const void* o, 
   return hip_status(fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on device `dev`.
+int scratch_address(int dev, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return FA_OK;
+}
+
 // Mask arguments: mask_block is checked first (so a bad block size is
 // reported even for empty shapes), then a non-empty problem needs a mask.
 int check_mask(int B, int H, int N, const uint8_t* block_mask, int mask_block) {
@@ -194,6 +228,27 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                          N, d, scale, causal, nullptr, 0, stream);
 }
 
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                        int B, int H, int N, int d, float scale, int causal, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dout) ||
+      !tensor_ok(dq) || !tensor_ok(dk) || !tensor_ok(dv))
+    return FA_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (workspace_size(B, H, N, d) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = -1;
+  if ((s == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(s, &dev)) != hipSuccess)
+    return FA_ERR_HIP;
+  void* ws = nullptr;
+  if ((st = scratch_address(dev, &ws)) != FA_OK) return st;
+  return backward_common(q, k, v, o, dout, lse, dq, dk, dv, ws, FA_NOALLOC_SCRATCH_BYTES, B, H,
+                         H, N, d, scale, causal, nullptr, 0, stream);
+}
+
 int fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, float* dq, float* dk, float* dv,
                             void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
@@ -222,6 +277,7 @@ const char* fa_error_string(int status) {
     case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or scale)";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; mask block 128)";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
+    case FA_ERR_TOO_LARGE: return "problem too large for the fixed no-allocation scratch (B*H*N <= 1048576 rows)";
     default: return "unknown status";
   }
 }

@@ -18,8 +18,10 @@
  *  Memory     every tensor pointer is a DEVICE pointer on the current HIP
  *             device; `block_mask` is a device pointer too.  The caller owns
  *             every buffer (inputs, outputs, workspace); the library never
- *             allocates or frees memory and keeps no global state, so it is
- *             re-entrant.  Buffers must not overlap.
+ *             allocates or frees memory, so it is re-entrant.  Buffers must
+ *             not overlap.  The one exception is fa_backward_noalloc, which
+ *             uses a fixed scratch array the library holds on each device
+ *             (see there).
  *  Streams    `stream` is a hipStream_t passed as void* (NULL = the null
  *             stream).  Calls are asynchronous: they enqueue kernels on the
  *             stream and return; buffers must stay alive until it syncs.
@@ -47,8 +49,12 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad scale, misalignment */
   FA_ERR_UNSUPPORTED = 2, /* valid request outside what is built (d, mask block) */
-  FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+  FA_ERR_TOO_LARGE = 4    /* the problem needs more than the fixed no-allocation scratch */
 } fa_status;
+
+/* Bytes of the fixed per-device scratch array of fa_backward_noalloc. */
+#define FA_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /*
  * Forward pass, bf16 storage, fp32 accumulation.
@@ -98,6 +104,29 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 const float* lse, float* dq, float* dk, float* dv, void* workspace,
                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                 void* stream);
+
+/*
+ * fa_backward for callers that cannot allocate memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid allocation): the same
+ * kernels and results as fa_backward, but the workspace (D and LSE * log2(e),
+ * two fp32 per row) lives in a fixed device array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on until the process ends.  The call itself allocates nothing.
+ *   Arguments as fa_backward without workspace / workspace_bytes.
+ *   Limit: fa_backward_workspace_size(B, H, N, d) <= FA_NOALLOC_SCRATCH_BYTES,
+ *          i.e. B * H * N <= 1048576 rows; larger problems return
+ *          FA_ERR_TOO_LARGE before anything is enqueued.
+ *   Device: the scratch of the device `stream` belongs to (the current device
+ *          for the null stream) is used; its address is looked up on the
+ *          first call on that device.
+ *   Races: every call on one GPU shares that GPU's scratch, so calls whose
+ *          kernels can overlap on one GPU (different streams without
+ *          ordering between them) race and must not be issued.  Each call
+ *          writes the scratch before reading it; nothing has to be cleared.
+ */
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                        int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
  * Block-sparse forward: like fa_forward, but scores in tiles whose mask entry

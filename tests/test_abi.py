@@ -40,8 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_error_strings():
     lib = _lib.load()
-    assert _lib.version() == 300
-    for st in range(4):
+    assert _lib.version() == 400
+    for st in range(5):
         s = _lib.error_string(st)
         assert isinstance(s, str) and s
     assert _lib.error_string(99) == "unknown status"
@@ -204,3 +204,28 @@ def test_gqa_workspace_size():
     assert gqa(1, 4, 0, 128, 64) == 0
     assert gqa(1, 4, 2, 128, 80) == 0
     assert gqa(1, 4, 2, 0, 64) == 0
+
+
+def test_noalloc_backward_argument_errors_and_limit():
+    """fa_backward_noalloc validates like fa_backward and refuses problems whose
+    workspace exceeds the fixed scratch before any HIP call."""
+    lib = _lib.load()
+    INV, BIG, OK = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_TOO_LARGE, _lib.FA_OK
+
+    def nb(B=1, H=1, N=16, d=64, q=FAKE, dq=FAKE, lse=FAKE, scale=0.125):
+        return lib.fa_backward_noalloc(q, FAKE, FAKE, FAKE, FAKE, lse, dq, FAKE, FAKE, B, H, N, d,
+                                       scale, 1, None)
+
+    assert nb(q=None) == INV
+    assert nb(dq=MIS) == INV
+    assert nb(lse=FAKE + 2) == INV
+    assert nb(scale=0.0) == INV
+    assert nb(d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert nb(q=None, dq=None, lse=None, N=0) == OK
+    rows = _lib.NOALLOC_SCRATCH_BYTES // 8  # two fp32 per row
+    assert rows == 1 << 20
+    assert _lib.backward_workspace_size(1, 1, rows, 64) == _lib.NOALLOC_SCRATCH_BYTES
+    assert nb(N=rows + 1) == BIG
+    assert nb(B=4, H=16, N=16385) == BIG
+    assert nb(B=4, H=16, N=16385, q=None) == INV  # pointers are checked first
+    assert "no-allocation" in _lib.error_string(BIG)
