@@ -192,6 +192,24 @@ def test_forward_eight_wave_grid(N, causal):
     forward_parity_all_heads(q, k, v, causal, chunk=130)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [700, 1500])
+def test_forward_reference_moves_mid_sequence(N, causal):
+    """Keys from the fourth 64-key tile on scaled by 3, so that those tiles'
+    scores exceed the running reference set by the first tiles by far more
+    than 2^3 per weight: the hand-scheduled d = 128 loop must take its exact
+    path (row maximum, rescale, recomputed weights) there, in the launch
+    configuration of the long workloads (B2 H130: more than one 256-row
+    workgroup per CU)."""
+    need_gpu()
+    log(f"forward bf16 B2 H130 N{N} d128 causal={causal}, keys x3 from key 192 on")
+    q, k, v = inputs.qkv(2, 130, N, 128, torch.bfloat16, seed=2000 + N)
+    kscale = torch.ones(N, dtype=torch.float32)
+    kscale[192:] = 3.0
+    k = (k.float() * kscale[None, None, :, None]).to(torch.bfloat16)
+    forward_parity_all_heads(q, k, v, causal, chunk=65)
+
+
 def test_caller_outputs_match_fresh_outputs():
     """forward/backward with caller-owned output buffers (out=) write exactly
     what they return with fresh ones, also over stale contents."""
