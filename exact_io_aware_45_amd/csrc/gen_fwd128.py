@@ -208,38 +208,60 @@ def p_reg(pbuf, rb, kb, cc):
     return P_BASE[pbuf] + 16 * rb + 8 * kb + 4 * cc
 
 
-def softmax_half(buf, pbuf, kb, fresh, tmp_ring, rbs=(0, 1)):
+SKEW = True   # software-pipeline the per-element chain across groups of four
+
+
+def softmax_half(buf, pbuf, kb, fresh, tmp_ring, rbs=(0, 1), skew=None):
     """Vector work of one 32-key half (kb) of a tile for the given row blocks:
     t = s * c - m; p = 2^t; ts[rb][r % 4] += p; P = bf16 pairs of p.
-    `fresh`: the first weight into each partial sum overwrites it."""
-    ops = []
+    `fresh`: the first weight into each partial sum overwrites it.
+
+    Elements go in groups of four (two pairs of neighbouring keys per row
+    block).  With SKEW the stream is software-pipelined: round k issues the
+    scaled differences of group k, the exponentials of group k - 1 and the
+    sums and packs of group k - 2, so every dependent instruction comes about
+    ten instructions after the one it waits for (an exponential's result is
+    not ready for several cycles)."""
     first = {(rb, i): fresh for rb in rbs for i in range(4)}
+    groups = []
     for g in range(8):            # pairs of elements r = 2g, 2g + 1
         elems = [(rb, 2 * g + e) for rb in rbs for e in range(2)]
-        tmps = {}
-        for (rb, r) in elems:
-            t = next(tmp_ring)
-            tmps[(rb, r)] = t
-            ops.append(Ins(f"v_fma_f32 {v(t)}, {v(s_reg(buf, rb, kb, r))}, s{S_C}, {v(MNEG + rb)}",
-                           "valu", [v(t)], [v(s_reg(buf, rb, kb, r)), v(MNEG + rb)]))
-        for (rb, r) in elems:
-            t = tmps[(rb, r)]
-            ops.append(Ins(f"v_exp_f32 {v(t)}, {v(t)}", "trans", [v(t)], [v(t)]))
+        tmps = {e: next(tmp_ring) for e in elems}
+        fma = [Ins(f"v_fma_f32 {v(tmps[(rb, r)])}, {v(s_reg(buf, rb, kb, r))}, s{S_C}, {v(MNEG + rb)}",
+                   "valu", [v(tmps[(rb, r)])], [v(s_reg(buf, rb, kb, r)), v(MNEG + rb)])
+               for (rb, r) in elems]
+        exp = [Ins(f"v_exp_f32 {v(tmps[e])}, {v(tmps[e])}", "trans", [v(tmps[e])], [v(tmps[e])])
+               for e in elems]
+        fin = []
         for (rb, r) in elems:
             t = tmps[(rb, r)]
             ts = TS + 4 * rb + (r % 4)
             if first[(rb, r % 4)]:
-                ops.append(Ins(f"v_mov_b32 {v(ts)}, {v(t)}", "valu", [v(ts)], [v(t)]))
+                fin.append(Ins(f"v_mov_b32 {v(ts)}, {v(t)}", "valu", [v(ts)], [v(t)]))
                 first[(rb, r % 4)] = False
             else:
-                ops.append(Ins(f"v_add_f32 {v(ts)}, {v(ts)}, {v(t)}", "valu", [v(ts)],
+                fin.append(Ins(f"v_add_f32 {v(ts)}, {v(ts)}, {v(t)}", "valu", [v(ts)],
                                [v(ts), v(t)]))
         for rb in rbs:
             r = 2 * g
             cc, i = r // 8, (r % 8) // 2
             dst = p_reg(pbuf, rb, kb, cc) + i
-            ops.append(Ins(f"v_cvt_pk_bf16_f32 {v(dst)}, {v(tmps[(rb, r)])}, {v(tmps[(rb, r + 1)])}",
+            fin.append(Ins(f"v_cvt_pk_bf16_f32 {v(dst)}, {v(tmps[(rb, r)])}, {v(tmps[(rb, r + 1)])}",
                            "valu", [v(dst)], [v(tmps[(rb, r)]), v(tmps[(rb, r + 1)])]))
+        groups.append((fma, exp, fin))
+    ops = []
+    if not (SKEW if skew is None else skew):
+        for fma, exp, fin in groups:
+            ops += fma + exp + fin
+        return ops
+    n = len(groups)
+    for k in range(n + 2):
+        if k < n:
+            ops += groups[k][0]
+        if 0 <= k - 1 < n:
+            ops += groups[k - 1][1]
+        if 0 <= k - 2 < n:
+            ops += groups[k - 2][2]
     return ops
 
 
@@ -423,10 +445,12 @@ def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, ta
         if k is not None:
             st.raw(f"s_waitcnt lgkmcnt({min(k, 15)})")
         st.emit(mf)
+        spent = 0.0
         for rid, ins in read_sched.get(i, []):
             st.emit(ins)
             lds.issue(rid)
-        fill(SLOT)
+            spent += ins.cost
+        fill(SLOT - spent)
     if tail_valu:
         for ins in valu:
             st.emit(ins)
@@ -524,8 +548,9 @@ def slow_path(st, cur, pcur, tmp_ring, back_label):
             for i in range(8):
                 st.emit(Ins(f"v_accvgpr_write_b32 {a(O_BASE + 64 * rb + base + i)}, {v(work[i])}",
                             "accw", [a(O_BASE + 64 * rb + base + i)], [v(work[i])]))
-    ring = tmp_cycle_from(TMP + 16, NTMP - 16 - 4)
-    for ins in softmax_half(cur, pcur, 0, True, ring) + softmax_half(cur, pcur, 1, False, ring):
+    ring = tmp_cycle_from(TMP + 16, NTMP - 16 - 4)   # four: one group at a time, unskewed
+    for ins in (softmax_half(cur, pcur, 0, True, ring, skew=False)
+                + softmax_half(cur, pcur, 1, False, ring, skew=False)):
         st.emit(ins)
     chk, tsums = check_ops()
     for ins in chk[:-2]:       # the sums only (no second test: every weight is now <= 1)
@@ -588,6 +613,9 @@ def entry(out):
     for o in range(3, 16):
         sched.setdefault(2 * (o - 3), []).append((("K", o), k_read(o, 0)))
     interleave(st, mf, before, [], lds, sched, need)
+    # every wave has read K_0 before iteration 0 loads K_2 into its stage
+    st.raw("s_waitcnt lgkmcnt(0)")
+    st.raw("s_barrier")
     # settle the products' results before the branch: both paths read them
     st.raw("s_nop 7", 8)
     st.raw("s_nop 7", 8)

@@ -499,9 +499,21 @@ def test_matrix_vector_hazards(path):
 
 
 def test_every_barrier_waits_for_the_direct_loads():
+    """A barrier that follows direct loads is preceded by vmcnt(0); the one
+    after the first tile's scores (no loads since the prologue's) waits for
+    the wave's LDS reads instead, so no wave reloads K stage 0 while another
+    still reads it."""
+    loads_since = False
     for i, l in enumerate(LINES):
+        if l.startswith("global_load_lds"):
+            loads_since = True
         if l == "s_barrier":
-            assert LINES[i - 1] == "s_waitcnt vmcnt(0)"
+            if loads_since or LINES[i - 1] != "s_waitcnt lgkmcnt(0)":
+                assert LINES[i - 1] == "s_waitcnt vmcnt(0)", i
+            loads_since = False
+    first = LINES.index("s_barrier")
+    assert LINES[first - 1] == "s_waitcnt lgkmcnt(0)"
+    assert not any(x.startswith("global_load_lds") for x in LINES[:first])
 
 
 def test_m0_set_one_state_before_each_direct_load():
