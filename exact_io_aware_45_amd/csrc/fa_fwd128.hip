@@ -41,11 +41,14 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd128_kernel(FwdArgs a) {
-  // LDS: V stage 0, V stage 1, K stage 0, K stage 1 (16 KiB each).  The
-  // generated loop addresses this map directly.
-  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
+  // LDS: V stage 0, V stage 1, K stage 0, K stage 1 (16 KiB each; the
+  // generated loop addresses this map directly), then the workgroup's 256
+  // query rows as four 64-row tiles (read once into registers).  After the
+  // loop each wave stages its normalised output rows in the first 64 KiB.
+  __shared__ __attribute__((aligned(1024))) bf16 smem[8 * TILE];
   auto Vst = [&](int stage) { return smem + stage * TILE; };
   auto Kst = [&](int stage) { return smem + (2 + stage) * TILE; };
+  auto Qst = [&](int i) { return smem + (4 + i) * TILE; };
   const uint32_t lds0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem));
 
@@ -62,7 +65,7 @@ void fwd128_kernel(FwdArgs a) {
   const int q0 = qt * BR;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -74,17 +77,7 @@ void fwd128_kernel(FwdArgs a) {
   const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + kvhead;
   bf16* __restrict__ O = reinterpret_cast<bf16*>(a.o) + head;
 
-  // Q^T operands: row block rb holds query rows q0 + 64 wave + 32 rb + l32,
-  // d = 16c + 8h .. +7.
   const int wrow0 = q0 + 64 * wave;
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = min(wrow0 + 32 * rb + l32, N - 1);
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      qf[rb][c] = *reinterpret_cast<const bf16x8*>(Q + (size_t)r * D + 16 * c + 8 * h);
-  }
 
   // Key tiles [0, tend); from tile fm on every tile needs a mask (the
   // causal diagonal tiles and a partial last tile).
@@ -162,12 +155,24 @@ void fwd128_kernel(FwdArgs a) {
     thr[rb] = __builtin_bit_cast(float, thri[rb]);
   }
 
-  // Prologue: K_0, V_0 and K_1 in flight together.
+  // Prologue: the workgroup's query rows, K_0, V_0 and K_1 in flight
+  // together, all by coalesced direct loads into swizzled tiles.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_tile(Q, q0 / BC + i, Qst(i));
   load_tile(K, 0, Kst(0));
   load_tile(V, 0, Vst(0));
   if (tend > 1) load_tile(K, 1, Kst(1));
   wait_global_loads();
   __syncthreads();
+
+  // Q^T operands: row block rb holds query rows q0 + 64 wave + 32 rb + l32,
+  // d = 16c + 8h .. +7 (rows past N - 1 repeat row N - 1; never stored).
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      qf[rb][c] = lds_read8(Qst(wave) + (32 * rb + l32) * D + 8 * ((2 * c + h) ^ sw_row));
 
   // Scalar operands (wave-uniform values, moved to SGPRs explicitly).
   auto uni = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); };
@@ -185,6 +190,7 @@ void fwd128_kernel(FwdArgs a) {
   uint32_t jt = 0;
   const uint32_t sfm = uni((uint32_t)fm);
   const uint32_t stail = uni((ragged && tend == nt) ? 1u : 0u);
+  const uint32_t ones = uni(0x3f803f80u);  // bf16 pair (1.0, 1.0)
   const uint32_t bperm = (uint32_t)((lane ^ 32) << 2);
   const float ninf = -INFINITY;
   float mneg0, mneg1, l0 = 0.f, l1 = 0.f;
@@ -206,32 +212,46 @@ void fwd128_kernel(FwdArgs a) {
                  "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
                  "{v[192:199]}"(kaddr), "{v[200:207]}"(vaddr), "{v[208:211]}"(goff),
                  "{v224}"(bperm), "{v251}"(ninf), "{v[252:255]}"(gtail),
-                 "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s70}"(sfm), "{s72}"(stail)
+                 "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s70}"(sfm), "{s72}"(stail),
+                 "{s82}"(ones)
                : FA_FWD128_LOOP_CLOBBERS);
   const float m_ref[2] = {-mneg0, -mneg1};
   const float lsum[2] = {l0, l1};
 
-  // Epilogue: O = acc / l (bf16), LSE = m + log2(l) in natural units.
+  // Epilogue: O = acc / l (bf16), LSE = m + log2(l) in natural units.  The
+  // loop ended with a barrier, so LDS is free: each wave writes its 64 rows
+  // into its own chunk-swizzled tile, then stores whole 16-byte row chunks
+  // (1 KiB of consecutive rows per store instruction).
+  // Lane values are taken afresh from the exec mask (the loop used every
+  // vector register).
+  const int el = __lane_id(), eh = el >> 5, e32 = el & 31;
+  bf16* ost = smem + wave * TILE;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int qrow = wrow0 + 32 * rb + l32;
+    const int qrow = wrow0 + 32 * rb + e32;
     const float l_tot = half_pair_sum(lsum[rb]);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qrow < N) {
-      if (h == 0)
-        a.lse[(size_t)bh * N + qrow] =
-            l_tot > 0.f ? (m_ref[rb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
-      bf16* orow = O + (size_t)qrow * D;
+    if (qrow < N && eh == 0)
+      a.lse[(size_t)bh * N + qrow] =
+          l_tot > 0.f ? (m_ref[rb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    const int row = 32 * rb + e32;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v4;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[rb][db][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = v4;
-        }
-    }
+        for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[rb][db][4 * g + e] * inv);
+        const int slot = (4 * db + g) ^ tile_swz<D>(row);
+        *reinterpret_cast<FA_LDS bf16x4*>((FA_LDS bf16*)ost + row * D + 8 * slot + 4 * eh) = v4;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 4 * i + (el >> 4), chunk = el & 15;
+    const bf16x8 v8 = lds_read8(ost + row * D + 8 * (chunk ^ tile_swz<D>(row)));
+    if (wrow0 + row < N)
+      *reinterpret_cast<bf16x8*>(O + (size_t)(wrow0 + row) * D + 8 * chunk) = v8;
   }
 }
 

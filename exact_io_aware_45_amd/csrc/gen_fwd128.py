@@ -54,8 +54,12 @@ OUT = os.path.join(HERE, "fa_fwd128_loop.inc")
 # AGPRs
 O_BASE = 0        # a[0:127]   O^T accumulators: O[rb][db] = a[64 rb + 16 db : +16]
 Q_BASE = 128      # a[128:191] Q^T operands:     Q[rb][c]  = a[128 + 32 rb + 4 c : +4]
-KR_BASE = 192     # a[192:207] K operand ring, 4 slots of 4
-VR_BASE = 208     # a[208:223] V^T operand ring, 4 slots of 4
+KRING = 8         # K operand ring slots (4 registers each)
+VRING = 8         # V^T operand ring slots
+KAHEAD = 3        # K operands read ahead of their first product
+VAHEAD = 3        # V^T operands read ahead of their first product
+KR_BASE = 192     # a[192:223] K operand ring
+VR_BASE = 224     # a[224:255] V^T operand ring
 # VGPRs
 S_BASE = (0, 64)  # v[0:63], v[64:127]   scores S[rb][kb] = v[base + 32 rb + 16 kb : +16]
 P_BASE = (128, 160)  # v[128:159], v[160:191] packed weights P[rb][kb][cc] = v[base + 16 rb + 8 kb + 4 cc : +4]
@@ -64,7 +68,7 @@ VADDR = 200       # v[200:207] V^T LDS addresses (stage 0), index 2 db + hi
 GOFF = 208        # v[208:211] per-lane byte offsets of the 4 direct loads within a tile
 MNEG = 212        # v212, v213: -m (reference, log2 units) per row block
 LSUM = 214        # v214, v215: running row sums (this lane's keys) per row block
-TS = 216          # v[216:223] tile partial sums ts[rb][i] = v[216 + 4 rb + i]
+TS = 216          # v[216:219] tile partial sums ts[rb][i] = v[216 + 2 rb + i], i = 0, 1
 BPERM = 224       # v224: byte address lane ^ 32 for ds_bpermute (slow path)
 TMP = 225         # v[225:248] temporaries
 NTMP = 24
@@ -85,6 +89,7 @@ S_J = 71          # index of the current tile
 S_TAIL = 72       # nonzero: the last tile is partial (its loads use GOFF_TAIL)
 S_T = 73          # scratch
 S_MASK = (74, 76, 78, 80)   # SGPR pairs for element masks
+S_ONES = 82       # bf16 pair (1.0, 1.0): the row sums are dot products with it
 
 # LDS map (bytes): V stage 0 at 0, V stage 1 at 16 KiB, K stage 0 at 32 KiB,
 # K stage 1 at 48 KiB.  KADDR/VADDR hold stage-0 addresses; a stage adds 16 KiB.
@@ -94,13 +99,16 @@ TILE_BYTES = 64 * 256   # one 64-key tile of K or V in global memory
 THRESH = "0x43800000"   # 256.0: the per-lane tile sum that sends a tile to the slow path
 
 # Conservative issue-cycle costs used to fill the shadow of each product.
-COST = {"valu": 4.5, "trans": 8.0, "lds": 4.0, "salu": 1.0, "vmem": 4.0, "nop": 1.0}
+COST = {"valu": 4.5, "trans": 8.0, "dot": 4.5, "lds": 4.0, "salu": 1.0, "vmem": 4.0, "nop": 1.0}
 SLOT = 27.0   # vector/LDS issue cycles one wave can overlap with one product
 
 # Hazard distances (in issued instructions; s_nop N counts N+1).
 H_MFMA_TO_READ = 18   # product result -> vector/LDS/accvgpr read
 H_VALU_TO_MFMA = 4    # vector write -> product source read
 H_TRANS_TO_USE = 2    # exponential -> vector read
+H_DOT_TO_READ = 4     # dot product result -> any vector read (accumulation included)
+H_VALU_TO_DOT = 3     # vector write -> dot product source read
+H_SMASK = 3           # vector compare writing an SGPR mask -> vector read of the mask
 
 
 def v(i):
@@ -169,8 +177,14 @@ class Stream:
                 wait = max(wait, H_MFMA_TO_READ - dist)
             elif kind in ("valu", "trans", "accw") and ins.kind == "mfma":
                 wait = max(wait, H_VALU_TO_MFMA - dist)
-            elif kind == "trans" and ins.kind in ("valu", "trans"):
+            elif kind == "trans" and ins.kind in ("valu", "trans", "dot"):
                 wait = max(wait, H_TRANS_TO_USE - dist)
+            if r.startswith("s") and kind == "valu":
+                wait = max(wait, H_SMASK - dist)
+            if kind == "dot" and ins.kind != "mfma":
+                wait = max(wait, H_DOT_TO_READ - dist)
+            if kind in ("valu", "trans") and ins.kind == "dot":
+                wait = max(wait, H_VALU_TO_DOT - dist)
         return max(0, wait)
 
     def emit(self, ins):
@@ -209,20 +223,23 @@ def p_reg(pbuf, rb, kb, cc):
 
 
 SKEW = True   # software-pipeline the per-element chain across groups of four
+LOOKAHEAD = 8  # pending vector instructions the slot filler may pick from
+DOT_SUMS = False  # row sums by v_dot2_f32_bf16 on packed pairs (measured slower: the dot instruction costs far more issue than two adds)
 
 
 def softmax_half(buf, pbuf, kb, fresh, tmp_ring, rbs=(0, 1), skew=None):
     """Vector work of one 32-key half (kb) of a tile for the given row blocks:
-    t = s * c - m; p = 2^t; ts[rb][r % 4] += p; P = bf16 pairs of p.
-    `fresh`: the first weight into each partial sum overwrites it.
+    t = s * c - m; p = 2^t; P = bf16 pairs of p; ts[rb][g % 2] += the pair's
+    sum (v_dot2_f32_bf16 against (1, 1): the sum of exactly the rounded
+    weights the P V product uses, so the normalisation matches them).
+    `fresh`: the first pair into each partial sum overwrites it.
 
     Elements go in groups of four (two pairs of neighbouring keys per row
     block).  With SKEW the stream is software-pipelined: round k issues the
     scaled differences of group k, the exponentials of group k - 1 and the
-    sums and packs of group k - 2, so every dependent instruction comes about
-    ten instructions after the one it waits for (an exponential's result is
-    not ready for several cycles)."""
-    first = {(rb, i): fresh for rb in rbs for i in range(4)}
+    packs and sums of group k - 2, so every dependent instruction comes
+    several instructions after the one it waits for."""
+    first = {(rb, i): fresh for rb in rbs for i in range(2)}
     groups = []
     for g in range(8):            # pairs of elements r = 2g, 2g + 1
         elems = [(rb, 2 * g + e) for rb in rbs for e in range(2)]
@@ -232,23 +249,28 @@ def softmax_half(buf, pbuf, kb, fresh, tmp_ring, rbs=(0, 1), skew=None):
                for (rb, r) in elems]
         exp = [Ins(f"v_exp_f32 {v(tmps[e])}, {v(tmps[e])}", "trans", [v(tmps[e])], [v(tmps[e])])
                for e in elems]
-        fin = []
-        for (rb, r) in elems:
-            t = tmps[(rb, r)]
-            ts = TS + 4 * rb + (r % 4)
-            if first[(rb, r % 4)]:
-                fin.append(Ins(f"v_mov_b32 {v(ts)}, {v(t)}", "valu", [v(ts)], [v(t)]))
-                first[(rb, r % 4)] = False
-            else:
-                fin.append(Ins(f"v_add_f32 {v(ts)}, {v(ts)}, {v(t)}", "valu", [v(ts)],
-                               [v(ts), v(t)]))
+        pk, dots = [], []
         for rb in rbs:
             r = 2 * g
             cc, i = r // 8, (r % 8) // 2
             dst = p_reg(pbuf, rb, kb, cc) + i
-            fin.append(Ins(f"v_cvt_pk_bf16_f32 {v(dst)}, {v(tmps[(rb, r)])}, {v(tmps[(rb, r + 1)])}",
-                           "valu", [v(dst)], [v(tmps[(rb, r)]), v(tmps[(rb, r + 1)])]))
-        groups.append((fma, exp, fin))
+            pk.append(Ins(f"v_cvt_pk_bf16_f32 {v(dst)}, {v(tmps[(rb, r)])}, {v(tmps[(rb, r + 1)])}",
+                          "valu", [v(dst)], [v(tmps[(rb, r)]), v(tmps[(rb, r + 1)])]))
+            ts = TS + 2 * rb + (g % 2)
+            if DOT_SUMS:
+                acc = "0" if first[(rb, g % 2)] else v(ts)
+                dots.append(Ins(f"v_dot2_f32_bf16 {v(ts)}, {v(dst)}, s{S_ONES}, {acc}", "dot",
+                                [v(ts)], [v(dst)] + ([] if acc == "0" else [v(ts)])))
+            else:
+                for e in range(2):
+                    t = tmps[(rb, r + e)]
+                    if first[(rb, g % 2)] and e == 0:
+                        dots.append(Ins(f"v_mov_b32 {v(ts)}, {v(t)}", "valu", [v(ts)], [v(t)]))
+                    else:
+                        dots.append(Ins(f"v_add_f32 {v(ts)}, {v(ts)}, {v(t)}", "valu", [v(ts)],
+                                        [v(ts), v(t)]))
+            first[(rb, g % 2)] = False
+        groups.append((fma, exp, pk + dots))
     ops = []
     if not (SKEW if skew is None else skew):
         for fma, exp, fin in groups:
@@ -274,14 +296,11 @@ def tmp_cycle():
 
 def check_ops():
     """Per-lane tile sums, the slow-path test and the running-sum update."""
-    t0, t1, t2, t3 = TMP + NTMP - 4, TMP + NTMP - 3, TMP + NTMP - 2, TMP + NTMP - 1
+    t0, t1, t2 = TMP + NTMP - 4, TMP + NTMP - 3, TMP + NTMP - 2
     ops = []
-    for rb, (x, y) in enumerate(((t0, t1), (t2, t3))):
-        ops.append(Ins(f"v_add_f32 {v(x)}, {v(TS + 4 * rb)}, {v(TS + 4 * rb + 1)}", "valu",
-                       [v(x)], [v(TS + 4 * rb), v(TS + 4 * rb + 1)]))
-        ops.append(Ins(f"v_add_f32 {v(y)}, {v(TS + 4 * rb + 2)}, {v(TS + 4 * rb + 3)}", "valu",
-                       [v(y)], [v(TS + 4 * rb + 2), v(TS + 4 * rb + 3)]))
-        ops.append(Ins(f"v_add_f32 {v(x)}, {v(x)}, {v(y)}", "valu", [v(x)], [v(x), v(y)]))
+    for rb, x in enumerate((t0, t2)):
+        ops.append(Ins(f"v_add_f32 {v(x)}, {v(TS + 2 * rb)}, {v(TS + 2 * rb + 1)}", "valu",
+                       [v(x)], [v(TS + 2 * rb), v(TS + 2 * rb + 1)]))
     ops.append(Ins(f"v_max_f32 {v(t1)}, {v(t0)}, {v(t2)}", "valu", [v(t1)], [v(t0), v(t2)]))
     ops.append(Ins(f"v_cmp_lt_f32 vcc, {THRESH}, {v(t1)}", "valu", ["vcc"], [v(t1)]))
     return ops, (t0, t2)
@@ -336,12 +355,12 @@ def mask_ops(buf, kbs, rbs=(0, 1)):
             off = 32 * kb + 8 * (r // 4) + r % 4
             pr = S_MASK[i]
             ops.append(Ins(f"v_cmp_gt_i32_e64 s[{pr}:{pr + 1}], {off}, {v(THR + rb)}", "valu",
-                           [], [v(THR + rb)]))
+                           [f"s{pr}"], [v(THR + rb)]))
         for i, (rb, kb, r) in enumerate(grp):
             sr = s_reg(buf, rb, kb, r)
             pr = S_MASK[i]
             ops.append(Ins(f"v_cndmask_b32_e64 {v(sr)}, {v(sr)}, {v(NINF)}, s[{pr}:{pr + 1}]",
-                           "valu", [v(sr)], [v(sr), v(NINF)]))
+                           "valu", [v(sr)], [v(sr), v(NINF), f"s{pr}"]))
     return ops
 
 
@@ -351,9 +370,9 @@ def thr_step():
 
 
 def k_read(o, stage):
-    """K operand o = (c, kb) into ring slot o % 4."""
+    """K operand o = (c, kb) into ring slot o % KRING."""
     c, kb = o // 2, o % 2
-    slot = KR_BASE + 4 * (o % 4)
+    slot = KR_BASE + 4 * (o % KRING)
     off = STAGE_BYTES * stage + 8192 * kb
     return Ins(f"ds_read_b128 {ar(slot, 4)}, {v(KADDR + c)} offset:{off}", "lds",
                regs_a(slot, 4), [v(KADDR + c)])
@@ -361,10 +380,10 @@ def k_read(o, stage):
 
 def v_reads(o, stage):
     """V^T operand o = (block b = 2 kb + cc, db): two transpose reads into
-    ring slot o % 4 (rows of the block's first and second 8-key groups)."""
+    ring slot o % VRING (rows of the block's first and second 8-key groups)."""
     b, db = o // 4, o % 4
     kb, cc = b // 2, b % 2
-    slot = VR_BASE + 4 * (o % 4)
+    slot = VR_BASE + 4 * (o % VRING)
     off = STAGE_BYTES * stage + (32 * kb + 16 * cc) * 256
     return [Ins(f"ds_read_b64_tr_b16 {ar(slot + 2 * hi, 2)}, {v(VADDR + 2 * db + hi)} offset:{off}",
                 "lds", regs_a(slot + 2 * hi, 2), [v(VADDR + 2 * db + hi)]) for hi in range(2)]
@@ -376,7 +395,7 @@ def s_mfma(m, nxt):
     o = m // 2
     dst = s_reg(nxt, rb, kb, 0)
     src_c = "0" if c == 0 else vr(dst, 16)
-    slot = KR_BASE + 4 * (o % 4)
+    slot = KR_BASE + 4 * (o % KRING)
     q = Q_BASE + 32 * rb + 4 * c
     srcc = regs_v(dst, 16) if c else []
     return Ins(f"v_mfma_f32_32x32x16_bf16 {vr(dst, 16)}, {ar(slot, 4)}, {ar(q, 4)}, {src_c}",
@@ -389,7 +408,7 @@ def pv_mfma(m, pbuf):
     b, db, rb = m // 8, (m // 2) % 4, m % 2
     kb, cc = b // 2, b % 2
     o = m // 2
-    slot = VR_BASE + 4 * (o % 4)
+    slot = VR_BASE + 4 * (o % VRING)
     dst = O_BASE + 64 * rb + 16 * db
     p = p_reg(pbuf, rb, kb, cc)
     return Ins(f"v_mfma_f32_32x32x16_bf16 {ar(dst, 16)}, {ar(slot, 4)}, {vr(p, 4)}, {ar(dst, 16)}",
@@ -426,12 +445,25 @@ def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, ta
     operand_reads[i]: rids product i needs."""
     valu = list(valu)
 
+    def ready(i):
+        """Instruction i of the pending list can go now: no hazard wait, and no
+        data dependence on an earlier pending instruction (it neither reads
+        what they write nor writes what they read or write)."""
+        ins = valu[i]
+        if st.need(ins) > 0:
+            return False
+        for prev in valu[:i]:
+            if (ins.uses | ins.srcc) & prev.defs or ins.defs & (prev.uses | prev.srcc | prev.defs):
+                return False
+        return True
+
     def fill(budget):
         used = 0.0
-        while valu and used + valu[0].cost <= budget + 1e-9:
-            if st.need(valu[0]) > 0:
+        while valu:
+            pick = next((i for i in range(min(LOOKAHEAD, len(valu))) if ready(i)), None)
+            if pick is None or used + valu[pick].cost > budget + 1e-9:
                 break
-            ins = valu.pop(0)
+            ins = valu.pop(pick)
             st.emit(ins)
             used += ins.cost
 
@@ -468,12 +500,13 @@ def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring):
             st.emit(ins)
         return tsums
     mf = [s_mfma(m, nxt) for m in range(32)]
-    before = [(("K", o), k_read(o, kstage)) for o in range(3)]
+    before = [(("K", o), k_read(o, kstage)) for o in range(KAHEAD)]
     sched, need = {}, {}
-    for m in range(32):
-        need[m] = {("K", m // 2)}
-    for o in range(3, 16):   # operand o's read after product 2(o - 3)
-        sched.setdefault(2 * (o - 3), []).append((("K", o), k_read(o, kstage)))
+    for m in range(32):   # one wait per two operands
+        o = m // 2
+        need[m] = {("K", o), ("K", o + 1)} if o % 2 == 0 else {("K", o)}
+    for o in range(KAHEAD, 16):   # operand o's read after product 2(o - KAHEAD)
+        sched.setdefault(2 * (o - KAHEAD), []).append((("K", o), k_read(o, kstage)))
     interleave(st, mf, before, soft + chk, lds, sched, need)
     return tsums
 
@@ -486,13 +519,16 @@ def phase_b(st, lds, cur_p, vstage, nxt, pnxt, final, tmp_ring, prefetched, next
     if nextmask and not final:
         soft = mask_ops(nxt, (0,)) + soft + mask_ops(nxt, (1,)) + thr_step()
     sched, need = {}, {}
-    for m in range(32):
-        need[m] = {("V", m // 2, 0), ("V", m // 2, 1)}
-    for o in range(3, 16):
+    for m in range(32):   # one wait per two operands
+        o = m // 2
+        need[m] = ({("V", o, 0), ("V", o, 1), ("V", o + 1, 0), ("V", o + 1, 1)}
+                   if o % 2 == 0 else {("V", o, 0), ("V", o, 1)})
+    for o in range(VAHEAD, 16):
         reads = v_reads(o, vstage)
-        sched.setdefault(2 * (o - 3) + 1, []).extend([(("V", o, h), reads[h]) for h in range(2)])
+        sched.setdefault(2 * (o - VAHEAD) + 1, []).extend([(("V", o, h), reads[h])
+                                                           for h in range(2)])
     before = []
-    for o in range(3):
+    for o in range(VAHEAD):
         if o not in prefetched:
             reads = v_reads(o, vstage)
             before += [(("V", o, h), reads[h]) for h in range(2)]
@@ -581,7 +617,7 @@ def iteration(out, name, cur, nxt, kstage_read, vstage, kstage_load, vstage_load
     tsums = phase_a(st, lds, cur, pcur, nxt, kstage_read, final, tmp_ring)
     # V^T reads for the first products of phase B go out before the test
     pre = []
-    for o in range(3):
+    for o in range(VAHEAD):
         for h, ins in enumerate(v_reads(o, vstage)):
             st.emit(ins)
             lds.issue(("V", o, h))
@@ -606,12 +642,13 @@ def entry(out):
     st.raw("s_nop 4")
     lds = LdsCounter()
     mf = [s_mfma(m, 0) for m in range(32)]
-    before = [(("K", o), k_read(o, 0)) for o in range(3)]
+    before = [(("K", o), k_read(o, 0)) for o in range(KAHEAD)]
     sched, need = {}, {}
     for m in range(32):
-        need[m] = {("K", m // 2)}
-    for o in range(3, 16):
-        sched.setdefault(2 * (o - 3), []).append((("K", o), k_read(o, 0)))
+        o = m // 2
+        need[m] = {("K", o), ("K", o + 1)} if o % 2 == 0 else {("K", o)}
+    for o in range(KAHEAD, 16):
+        sched.setdefault(2 * (o - KAHEAD), []).append((("K", o), k_read(o, 0)))
     interleave(st, mf, before, [], lds, sched, need)
     # every wave has read K_0 before iteration 0 loads K_2 into its stage
     st.raw("s_waitcnt lgkmcnt(0)")
@@ -696,9 +733,9 @@ def generate():
 def clobbers():
     """Registers the statement overwrites that are not operands."""
     regs = [f"v{i}" for i in range(0, 192)]              # both S and both P buffers
-    regs += [f"v{i}" for i in range(TS, TS + 8)]
+    regs += [f"v{i}" for i in range(TS, TS + 4)]
     regs += [f"v{i}" for i in range(TMP, TMP + NTMP)]
-    regs += [f"a{i}" for i in range(KR_BASE, VR_BASE + 16)]
+    regs += [f"a{i}" for i in range(KR_BASE, VR_BASE + 4 * VRING)]
     regs += [f"s{i}" for i in range(S_T, 82)]
     regs += ["vcc", "scc", "m0", "memory"]
     return regs

@@ -292,6 +292,11 @@ def run_wave(m, lds, mem, pc):
                                       m.vread(args[3])))
         elif op == "v_mov_b32":
             m.vwrite(args[0], m.vread_u(args[1]))
+        elif op == "v_dot2_f32_bf16":
+            x, y = m.vread_u(args[1]), m.vread_u(args[2])
+            prod = (bf16_to_f32(x & 0xFFFF).astype(np.float64) * bf16_to_f32(y & 0xFFFF)
+                    + bf16_to_f32(x >> 16).astype(np.float64) * bf16_to_f32(y >> 16))
+            m.vwrite(args[0], (prod + m.vread(args[3])).astype(np.float32))
         elif op == "v_cvt_pk_bf16_f32":
             lo_, hi_ = bf16_bits(m.vread(args[1])), bf16_bits(m.vread(args[2]))
             m.vwrite(args[0], (lo_ | (hi_ << 16)).astype(np.uint32))
@@ -406,6 +411,7 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
         m.s[G.S_FM] = fm
         m.s[G.S_J] = 0
         m.s[G.S_TAIL] = 1 if (ragged and tend == nt) else 0
+        m.s[G.S_ONES] = 0x3F803F80
         waves.append([m, 0])
     while True:
         for wv in waves:

@@ -388,6 +388,8 @@ def classify(op):
         return "mfma"
     if op.startswith("v_exp"):
         return "trans"
+    if op.startswith("v_dot"):
+        return "dot"
     if op.startswith("ds_"):
         return "lds"
     if op.startswith("v_"):
@@ -460,14 +462,16 @@ def test_matrix_vector_hazards(path):
     """Wait states (instructions issued; s_nop n counts n + 1) between a
     product writing a register and a vector/LDS instruction reading it >= 12
     (gfx950, 8-pass 32x32x16 product), between a vector write and a product
-    reading it >= 2, between an exponential and its reader >= 1."""
+    reading it >= 2, between an exponential and its reader >= 1, between a
+    dot product and any reader of its result (its own accumulation included)
+    >= 3, between a vector write and a dot product reading it >= 2."""
     body = straight_paths()[path]
     t = 0
     last = {}   # reg -> (kind, time)
     for l in body:
         op, args = split(l)
         kind = classify(op)
-        if kind in ("mfma", "valu", "trans", "lds"):
+        if kind in ("mfma", "valu", "trans", "lds", "dot"):
             if kind == "mfma":
                 reads = set(regs(args[1])) | set(regs(args[2])) | set(regs(args[3]))
                 writes = set(regs(args[0]))
@@ -475,6 +479,10 @@ def test_matrix_vector_hazards(path):
                 reads, writes = set(regs(args[1])), set(regs(args[0]))
             elif op == "v_cmp_lt_f32":
                 reads, writes = set(regs(args[2])), set()
+            elif op == "v_cmp_gt_i32_e64":
+                reads, writes = set(regs(args[2])), {args[0]}
+            elif op == "v_cndmask_b32_e64":
+                reads, writes = set(regs(args[1])) | set(regs(args[2])) | {args[3]}, set(regs(args[0]))
             else:
                 reads = set()
                 for x in args[1:]:
@@ -491,8 +499,14 @@ def test_matrix_vector_hazards(path):
                     assert dist >= 12, (l, r, dist)
                 if pk in ("valu", "trans") and kind == "mfma":
                     assert dist >= 2, (l, r, dist)
-                if pk == "trans" and kind in ("valu", "trans"):
+                if pk == "trans" and kind in ("valu", "trans", "dot"):
                     assert dist >= 1, (l, r, dist)
+                if pk == "dot" and kind != "mfma":
+                    assert dist >= 3, (l, r, dist)
+                if r.startswith("s[") and pk == "valu":
+                    assert dist >= 2, (l, r, dist)   # compare -> mask read
+                if pk in ("valu", "trans") and kind == "dot":
+                    assert dist >= 2, (l, r, dist)
             for r in writes:
                 last[r] = (kind, t)
         t += wait_states(l)
