@@ -131,16 +131,19 @@ void fwd128_kernel(FwdArgs a) {
     vaddr[2 * db] = lds0 + 2u * tr_off(tr_row, sw_lo, db);
     vaddr[2 * db + 1] = lds0 + 2u * tr_off(tr_row + 8, sw_hi, db);
   }
-  // Direct-load offsets within a tile, and for the partial last tile with
-  // its rows clamped to the sequence.
+  // Direct-load offsets within a tile (wave w loads rows 16w .. 16w + 15,
+  // four rows per load; load i carries instruction offset 1024 i, which
+  // applies to both the global and the LDS address, so it is taken off
+  // here), and for the partial last tile with its rows clamped to the
+  // sequence (absolute: those loads move M0 instead).
   u32x4 goff, gtail;
   const int tlast = tend - 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
+    const int p = (4 * wave + i) * 64 + lane;
     const int row = p >> 4;
     const int col = 8 * ((p & 15) ^ tile_swz<D>(row));
-    goff[i] = (uint32_t)(row * D + col) * 2u;
+    goff[i] = (uint32_t)(row * D + col) * 2u - 1024u * i;
     gtail[i] = (uint32_t)((min(tlast * BC + row, N - 1) - tlast * BC) * D + col) * 2u;
   }
   // Mask thresholds for tile fm: a score is masked when its key exceeds the
@@ -179,18 +182,24 @@ void fwd128_kernel(FwdArgs a) {
   auto uni64 = [&](uint64_t x) {
     return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x);
   };
-  const uint32_t m0k = uni(lds0 + 2 * TILE * 2 + wave * 1024);
-  const uint32_t m0v = uni(lds0 + wave * 1024);
+  const uint32_t m0k = uni(lds0 + 2 * TILE * 2 + wave * 4096);
+  const uint32_t m0v = uni(lds0 + wave * 4096);
   const uint32_t cbits = uni(__builtin_bit_cast(uint32_t, sl2));
   uint64_t kptr = uni64(reinterpret_cast<uint64_t>(K + 2 * (size_t)TILE));
   uint64_t vptr = uni64(reinterpret_cast<uint64_t>(V + 1 * (size_t)TILE));
-  uint32_t iters = uni((uint32_t)(tend - 1));
-  uint32_t nk = uni((uint32_t)max(0, tend - 2));
-  uint32_t nv = uni((uint32_t)max(0, tend - 1));
+  // Loop control: iteration j processes tile j and loads K_{j+2} and
+  // V_{j+1}; the partial last tile (loaded by iteration nt - 3 for K, nt - 2
+  // for V) goes through the clamped offsets; iterations below `sfast` have
+  // an unmasked next tile and two whole loads.
+  const bool tail = ragged && tend == nt;
+  const int kfull = tail ? nt - 1 : tend;
   uint32_t jt = 0;
+  const uint32_t slast = uni((uint32_t)(tend - 1));
+  const uint32_t skend = uni((uint32_t)max(0, tend - 2));
+  const uint32_t sktail = uni(tail && nt >= 3 ? (uint32_t)(nt - 3) : ~0u);
+  const uint32_t svtail = uni(tail && nt >= 2 ? (uint32_t)(nt - 2) : ~0u);
   const uint32_t sfm = uni((uint32_t)fm);
-  const uint32_t stail = uni((ragged && tend == nt) ? 1u : 0u);
-  const uint32_t ones = uni(0x3f803f80u);  // bf16 pair (1.0, 1.0)
+  const uint32_t sfast = uni((uint32_t)max(0, min(fm - 1, kfull - 2)));
   const uint32_t bperm = (uint32_t)((lane ^ 32) << 2);
   const float ninf = -INFINITY;
   float mneg0, mneg1, l0 = 0.f, l1 = 0.f;
@@ -200,8 +209,7 @@ void fwd128_kernel(FwdArgs a) {
                  "+{a[96:111]}"(o[1][2]), "+{a[112:127]}"(o[1][3]),
                  "={v212}"(mneg0), "={v213}"(mneg1), "+{v214}"(l0), "+{v215}"(l1),
                  "+{v249}"(thr[0]), "+{v250}"(thr[1]),
-                 "+{s[60:61]}"(kptr), "+{s[62:63]}"(vptr), "+{s67}"(iters), "+{s68}"(nk),
-                 "+{s69}"(nv), "+{s71}"(jt)
+                 "+{s[60:61]}"(kptr), "+{s[62:63]}"(vptr), "+{s71}"(jt)
                : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]),
                  "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
                  "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]),
@@ -212,46 +220,50 @@ void fwd128_kernel(FwdArgs a) {
                  "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
                  "{v[192:199]}"(kaddr), "{v[200:207]}"(vaddr), "{v[208:211]}"(goff),
                  "{v224}"(bperm), "{v251}"(ninf), "{v[252:255]}"(gtail),
-                 "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s70}"(sfm), "{s72}"(stail),
-                 "{s82}"(ones)
+                 "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s67}"(slast), "{s68}"(skend),
+                 "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast)
                : FA_FWD128_LOOP_CLOBBERS);
   const float m_ref[2] = {-mneg0, -mneg1};
   const float lsum[2] = {l0, l1};
 
   // Epilogue: O = acc / l (bf16), LSE = m + log2(l) in natural units.  The
   // loop ended with a barrier, so LDS is free: each wave writes its 64 rows
-  // into its own chunk-swizzled tile, then stores whole 16-byte row chunks
-  // (1 KiB of consecutive rows per store instruction).
-  // Lane values are taken afresh from the exec mask (the loop used every
-  // vector register).
+  // into its own tile with rows padded to 272 bytes (both the 8-byte writes
+  // of 32 rows and the 16-byte reads of 4 whole rows then touch every bank
+  // equally often), and stores whole rows, 1 KiB of consecutive rows per
+  // store instruction.  Lane values are taken afresh from the exec mask (the
+  // loop used every vector register).
+  constexpr int OST = D + 8;
   const int el = __lane_id(), eh = el >> 5, e32 = el & 31;
-  bf16* ost = smem + wave * TILE;
+  FA_LDS bf16* ost = (FA_LDS bf16*)(smem + wave * (64 * OST));
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int qrow = wrow0 + 32 * rb + e32;
-    const float l_tot = half_pair_sum(lsum[rb]);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qrow < N && eh == 0)
-      a.lse[(size_t)bh * N + qrow] =
-          l_tot > 0.f ? (m_ref[rb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
-    const int row = 32 * rb + e32;
+    const float l_tot = lsum[rb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                 (el ^ 32) << 2, __builtin_bit_cast(int, lsum[rb])));
+    const float inv = __builtin_amdgcn_rcpf(l_tot);
+    if (qrow < N && eh == 0) a.lse[(size_t)bh * N + qrow] = (m_ref[rb] + fast_log2(l_tot)) * kLn2;
+    FA_LDS bf16* orow = ost + (32 * rb + e32) * OST + 4 * eh;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int c = 0; c < 16; ++c) {
+      bf16x4 v4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[rb][db][4 * g + e] * inv);
-        const int slot = (4 * db + g) ^ tile_swz<D>(row);
-        *reinterpret_cast<FA_LDS bf16x4*>((FA_LDS bf16*)ost + row * D + 8 * slot + 4 * eh) = v4;
-      }
+      for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[rb][c >> 2][4 * (c & 3) + e] * inv);
+      *reinterpret_cast<FA_LDS bf16x4*>(orow + 8 * c) = v4;
+    }
   }
+  const FA_LDS bf16* src = ost + (el >> 4) * OST + 8 * (el & 15);
+  bf16* dst = O + (size_t)(wrow0 + (el >> 4)) * D + 8 * (el & 15);
+  if (wrow0 + 64 <= N) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 4 * i + (el >> 4), chunk = el & 15;
-    const bf16x8 v8 = lds_read8(ost + row * D + 8 * (chunk ^ tile_swz<D>(row)));
-    if (wrow0 + row < N)
-      *reinterpret_cast<bf16x8*>(O + (size_t)(wrow0 + row) * D + 8 * chunk) = v8;
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<bf16x8*>(dst + 4 * i * D) = *reinterpret_cast<const FA_LDS bf16x8*>(src + 4 * i * OST);
+  } else {
+    const int rows = N - wrow0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (4 * i + (el >> 4) < rows)
+        *reinterpret_cast<bf16x8*>(dst + 4 * i * D) = *reinterpret_cast<const FA_LDS bf16x8*>(src + 4 * i * OST);
   }
 }
 

@@ -81,15 +81,16 @@ S_VPTR = 62       # s[62:63] global address of the next V tile to load
 S_M0K = 64        # LDS address of this wave's first K load (stage 0)
 S_M0V = 65        # LDS address of this wave's first V load (stage 0)
 S_C = 66          # scale * log2(e) (fp32 bits)
-S_ITER = 67       # pipelined iterations left
-S_NK = 68         # K tiles left to load
-S_NV = 69         # V tiles left to load
+S_LAST = 67       # index of the last tile: its iteration is the final one
+S_KEND = 68       # iterations j >= this load no K tile (tile j + 2 does not exist)
+S_KTAILJ = 69     # iteration whose K load is the partial last tile (~0 when none)
 S_FM = 70         # first tile that needs a mask (tend when none)
 S_J = 71          # index of the current tile
-S_TAIL = 72       # nonzero: the last tile is partial (its loads use GOFF_TAIL)
+S_VTAILJ = 72     # iteration whose V load is the partial last tile (~0 when none)
 S_T = 73          # scratch
 S_MASK = (74, 76, 78, 80)   # SGPR pairs for element masks
-S_ONES = 82       # bf16 pair (1.0, 1.0): the row sums are dot products with it
+S_FAST = 82       # iterations j < this take the straight body: tile j + 1 needs no
+                  # mask and both of its loads are whole tiles
 
 # LDS map (bytes): V stage 0 at 0, V stage 1 at 16 KiB, K stage 0 at 32 KiB,
 # K stage 1 at 48 KiB.  KADDR/VADDR hold stage-0 addresses; a stage adds 16 KiB.
@@ -99,15 +100,13 @@ TILE_BYTES = 64 * 256   # one 64-key tile of K or V in global memory
 THRESH = "0x43800000"   # 256.0: the per-lane tile sum that sends a tile to the slow path
 
 # Conservative issue-cycle costs used to fill the shadow of each product.
-COST = {"valu": 4.5, "trans": 8.0, "dot": 4.5, "lds": 4.0, "salu": 1.0, "vmem": 4.0, "nop": 1.0}
+COST = {"valu": 4.5, "trans": 8.0, "lds": 4.0, "salu": 4.0, "vmem": 4.0, "nop": 1.0}
 SLOT = 27.0   # vector/LDS issue cycles one wave can overlap with one product
 
 # Hazard distances (in issued instructions; s_nop N counts N+1).
 H_MFMA_TO_READ = 18   # product result -> vector/LDS/accvgpr read
 H_VALU_TO_MFMA = 4    # vector write -> product source read
 H_TRANS_TO_USE = 2    # exponential -> vector read
-H_DOT_TO_READ = 4     # dot product result -> any vector read (accumulation included)
-H_VALU_TO_DOT = 3     # vector write -> dot product source read
 H_SMASK = 3           # vector compare writing an SGPR mask -> vector read of the mask
 
 
@@ -177,14 +176,10 @@ class Stream:
                 wait = max(wait, H_MFMA_TO_READ - dist)
             elif kind in ("valu", "trans", "accw") and ins.kind == "mfma":
                 wait = max(wait, H_VALU_TO_MFMA - dist)
-            elif kind == "trans" and ins.kind in ("valu", "trans", "dot"):
+            elif kind == "trans" and ins.kind in ("valu", "trans"):
                 wait = max(wait, H_TRANS_TO_USE - dist)
             if r.startswith("s") and kind == "valu":
                 wait = max(wait, H_SMASK - dist)
-            if kind == "dot" and ins.kind != "mfma":
-                wait = max(wait, H_DOT_TO_READ - dist)
-            if kind in ("valu", "trans") and ins.kind == "dot":
-                wait = max(wait, H_VALU_TO_DOT - dist)
         return max(0, wait)
 
     def emit(self, ins):
@@ -224,15 +219,15 @@ def p_reg(pbuf, rb, kb, cc):
 
 SKEW = True   # software-pipeline the per-element chain across groups of four
 LOOKAHEAD = 8  # pending vector instructions the slot filler may pick from
-DOT_SUMS = False  # row sums by v_dot2_f32_bf16 on packed pairs (measured slower: the dot instruction costs far more issue than two adds)
 
 
 def softmax_half(buf, pbuf, kb, fresh, tmp_ring, rbs=(0, 1), skew=None):
     """Vector work of one 32-key half (kb) of a tile for the given row blocks:
-    t = s * c - m; p = 2^t; P = bf16 pairs of p; ts[rb][g % 2] += the pair's
-    sum (v_dot2_f32_bf16 against (1, 1): the sum of exactly the rounded
-    weights the P V product uses, so the normalisation matches them).
-    `fresh`: the first pair into each partial sum overwrites it.
+    t = s * c - m; p = 2^t; P = bf16 pairs of p; ts[rb][g % 2] += both fp32
+    weights of the pair (two adds: a bf16 dot product against (1, 1) sums
+    the rounded weights in one instruction, but it issues far slower and
+    needs extra wait states before its result is read).
+    `fresh`: the first weight into each partial sum overwrites it.
 
     Elements go in groups of four (two pairs of neighbouring keys per row
     block).  With SKEW the stream is software-pipelined: round k issues the
@@ -257,18 +252,13 @@ def softmax_half(buf, pbuf, kb, fresh, tmp_ring, rbs=(0, 1), skew=None):
             pk.append(Ins(f"v_cvt_pk_bf16_f32 {v(dst)}, {v(tmps[(rb, r)])}, {v(tmps[(rb, r + 1)])}",
                           "valu", [v(dst)], [v(tmps[(rb, r)]), v(tmps[(rb, r + 1)])]))
             ts = TS + 2 * rb + (g % 2)
-            if DOT_SUMS:
-                acc = "0" if first[(rb, g % 2)] else v(ts)
-                dots.append(Ins(f"v_dot2_f32_bf16 {v(ts)}, {v(dst)}, s{S_ONES}, {acc}", "dot",
-                                [v(ts)], [v(dst)] + ([] if acc == "0" else [v(ts)])))
-            else:
-                for e in range(2):
-                    t = tmps[(rb, r + e)]
-                    if first[(rb, g % 2)] and e == 0:
-                        dots.append(Ins(f"v_mov_b32 {v(ts)}, {v(t)}", "valu", [v(ts)], [v(t)]))
-                    else:
-                        dots.append(Ins(f"v_add_f32 {v(ts)}, {v(ts)}, {v(t)}", "valu", [v(ts)],
-                                        [v(ts), v(t)]))
+            for e in range(2):
+                t = tmps[(rb, r + e)]
+                if first[(rb, g % 2)] and e == 0:
+                    dots.append(Ins(f"v_mov_b32 {v(ts)}, {v(t)}", "valu", [v(ts)], [v(t)]))
+                else:
+                    dots.append(Ins(f"v_add_f32 {v(ts)}, {v(ts)}, {v(t)}", "valu", [v(ts)],
+                                    [v(ts), v(t)]))
             first[(rb, g % 2)] = False
         groups.append((fma, exp, pk + dots))
     ops = []
@@ -311,34 +301,58 @@ def lsum_ops(tsums):
                 [v(LSUM + rb)], [v(LSUM + rb), v(tsums[rb])]) for rb in range(2)]
 
 
-def load_block(st, which, stage, uid):
-    """Direct HBM -> LDS loads of one K or V tile (4 per wave), if any are
-    left; the last one of a sequence with a partial last tile uses the
-    clamped offsets.  Advances the pointer and the count."""
-    sptr, sm0, scnt = (S_KPTR, S_M0K, S_NK) if which == "K" else (S_VPTR, S_M0V, S_NV)
+def full_loads(which, stage):
+    """Direct HBM -> LDS loads of one whole K or V tile into `stage`: M0 is
+    the wave's base in the stage and load i fills LDS [M0 + 1024 i, +1024)
+    from offsets GOFF + i, which have 1024 i taken off (the instruction
+    offset is added to both addresses).  Returns (M0 set-up, the four loads,
+    the pointer step to the next tile); M0 must be written at least one
+    instruction before the first load."""
+    sptr, sm0 = (S_KPTR, S_M0K) if which == "K" else (S_VPTR, S_M0V)
+    pre = [f"s_add_u32 m0, s{sm0}, {STAGE_BYTES * stage}"]
+    loads = [f"global_load_lds_dwordx4 {v(GOFF + i)}, s[{sptr}:{sptr + 1}] offset:{1024 * i}"
+             for i in range(4)]
+    post = [f"s_add_u32 s{sptr}, s{sptr}, {TILE_BYTES}", f"s_addc_u32 s{sptr + 1}, s{sptr + 1}, 0"]
+    return pre, loads, post
+
+
+def tail_loads(which, stage):
+    """Loads of the partial last tile: offsets with the rows clamped to the
+    sequence (absolute, so M0 carries the 1024 i)."""
+    sptr, sm0 = (S_KPTR, S_M0K) if which == "K" else (S_VPTR, S_M0V)
+    out = []
+    for i in range(4):
+        out += [f"s_add_u32 m0, s{sm0}, {STAGE_BYTES * stage + 1024 * i}", "s_nop 0",
+                f"global_load_lds_dwordx4 {v(GOFF_TAIL + i)}, s[{sptr}:{sptr + 1}]"]
+    return out
+
+
+def load_block(st, which, stage, uid, can_skip, can_tail):
+    """The loads of a body other than the straight one, before its products:
+    none when the tile does not exist (K only: tile j + 2 past the end), the
+    clamped ones for the partial last tile, else the whole tile."""
     skip = f"FA_SKIP{which}{uid}_%="
     tail = f"FA_TAIL{which}{uid}_%="
     done = f"FA_LDONE{which}{uid}_%="
-    st.raw(f"s_cmp_eq_u32 s{scnt}, 0")
-    st.raw(f"s_cbranch_scc1 {skip}")
-    st.raw(f"s_cmp_eq_u32 s{scnt}, 1")
-    st.raw(f"s_cselect_b32 s{S_T}, s{S_TAIL}, 0")
-    st.raw(f"s_cmp_lg_u32 s{S_T}, 0")
-    st.raw(f"s_cbranch_scc1 {tail}")
-    for offs, lbl in ((GOFF, None), (GOFF_TAIL, tail)):
-        if lbl:
-            st.label(lbl)
-        for i in range(4):
-            st.raw(f"s_add_u32 m0, s{sm0}, {4096 * i + STAGE_BYTES * stage}")
-            st.raw("s_nop 0")
-            st.raw(f"global_load_lds_dwordx4 {v(offs + i)}, s[{sptr}:{sptr + 1}]")
-        if not lbl:
-            st.raw(f"s_branch {done}")
-    st.label(done)
-    st.raw(f"s_add_u32 s{sptr}, s{sptr}, {TILE_BYTES}")
-    st.raw(f"s_addc_u32 s{sptr + 1}, s{sptr + 1}, 0")
-    st.raw(f"s_sub_u32 s{scnt}, s{scnt}, 1")
-    st.label(skip)
+    if can_skip:
+        st.raw(f"s_cmp_ge_u32 s{S_J}, s{S_KEND}")
+        st.raw(f"s_cbranch_scc1 {skip}")
+    if can_tail:
+        st.raw(f"s_cmp_eq_u32 s{S_J}, s{S_KTAILJ if which == 'K' else S_VTAILJ}")
+        st.raw(f"s_cbranch_scc1 {tail}")
+    pre, loads, post = full_loads(which, stage)
+    for l in pre + ["s_nop 0"] + loads:
+        st.raw(l)
+    if can_tail:
+        st.raw(f"s_branch {done}")
+        st.label(tail)
+        for l in tail_loads(which, stage):
+            st.raw(l)
+        st.label(done)
+    for l in post:
+        st.raw(l)
+    if can_skip:
+        st.label(skip)
 
 
 def mask_ops(buf, kbs, rbs=(0, 1)):
@@ -437,12 +451,15 @@ class LdsCounter:
         return k
 
 
-def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, tail_valu=True):
+def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, tail_valu=True,
+               raw_sched=None):
     """Emit the products in order; after product i, the LDS reads scheduled
-    for it, then vector work up to the slot budget.  `reads_before` are
-    issued first (with some vector work after them to cover their latency).
+    for it, the scalar/load lines raw_sched[i], then vector work up to the
+    slot budget.  `reads_before` are issued first (with some vector work
+    after them to cover their latency).
     read_sched[i]: list of (rid, Ins) issued after product i.
     operand_reads[i]: rids product i needs."""
+    raw_sched = raw_sched or {}
     valu = list(valu)
 
     def ready(i):
@@ -482,6 +499,9 @@ def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, ta
             st.emit(ins)
             lds.issue(rid)
             spent += ins.cost
+        for line in raw_sched.get(i, []):
+            st.raw(line)
+            spent += COST["vmem"] if line.startswith("global_") else COST["salu"]
         fill(SLOT - spent)
     if tail_valu:
         for ins in valu:
@@ -490,7 +510,7 @@ def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, ta
     return valu
 
 
-def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring):
+def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring, raw_sched=None):
     """Scores of the next tile (32 products) beside the second half of the
     current tile's weights, then the sum test.  Returns the tile-sum regs."""
     soft = softmax_half(cur, pcur, 1, False, tmp_ring)
@@ -507,7 +527,7 @@ def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring):
         need[m] = {("K", o), ("K", o + 1)} if o % 2 == 0 else {("K", o)}
     for o in range(KAHEAD, 16):   # operand o's read after product 2(o - KAHEAD)
         sched.setdefault(2 * (o - KAHEAD), []).append((("K", o), k_read(o, kstage)))
-    interleave(st, mf, before, soft + chk, lds, sched, need)
+    interleave(st, mf, before, soft + chk, lds, sched, need, raw_sched=raw_sched)
     return tsums
 
 
@@ -604,17 +624,30 @@ def tmp_cycle_from(lo, n):
         i += 1
 
 
-def iteration(out, name, cur, nxt, kstage_read, vstage, kstage_load, vstage_load, final,
-              nextmask=False):
+def iteration(out, name, cur, nxt, kstage_read, vstage, kstage_load, vstage_load, kind):
     """One tile step: loads, phase A, test, phase B, barrier.  `name` makes
-    the labels unique within the statement."""
+    the labels unique within the statement.  kind: "fast" (the straight
+    body: whole loads spread over the first products, the tile counter
+    stepped and compared there too, leaving SCC = the next step is straight
+    as well), "gen" (next tile unmasked, loads decided by the tile index),
+    "masked" (next tile masked) or "final" (no next tile, no loads)."""
     st = Stream(out)
     lds = LdsCounter()
     tmp_ring = tmp_cycle_from(TMP, NTMP - 4)
     pcur, pnxt = cur, nxt
-    load_block(st, "K", kstage_load, name)
-    load_block(st, "V", vstage_load, name)
-    tsums = phase_a(st, lds, cur, pcur, nxt, kstage_read, final, tmp_ring)
+    final = kind == "final"
+    raw_sched = None
+    if kind == "fast":
+        kpre, kloads, kpost = full_loads("K", kstage_load)
+        vpre, vloads, vpost = full_loads("V", vstage_load)
+        step = [f"s_add_u32 s{S_J}, s{S_J}, 1", f"s_cmp_lt_u32 s{S_J}, s{S_FAST}"]
+        raw_sched = {0: kpre, 1: kloads[:1], 2: kloads[1:2], 3: kloads[2:3],
+                     4: kloads[3:] + kpost + vpre, 5: vloads[:1], 6: vloads[1:2],
+                     7: vloads[2:3], 8: vloads[3:] + vpost + step}
+    elif kind in ("gen", "masked"):
+        load_block(st, "K", kstage_load, name, can_skip=True, can_tail=True)
+        load_block(st, "V", vstage_load, name, can_skip=False, can_tail=kind == "masked")
+    tsums = phase_a(st, lds, cur, pcur, nxt, kstage_read, final, tmp_ring, raw_sched)
     # V^T reads for the first products of phase B go out before the test
     pre = []
     for o in range(VAHEAD):
@@ -628,7 +661,7 @@ def iteration(out, name, cur, nxt, kstage_read, vstage, kstage_load, vstage_load
     for ins in lsum_ops(tsums):
         st.emit(ins)
     st.label(back_lbl)
-    phase_b(st, lds, pcur, vstage, nxt, pnxt, final, tmp_ring, pre, nextmask)
+    phase_b(st, lds, pcur, vstage, nxt, pnxt, final, tmp_ring, pre, kind == "masked")
     st.raw("s_waitcnt vmcnt(0)")
     st.raw("s_barrier")
     return slow_lbl, back_lbl, cur, pcur
@@ -687,37 +720,45 @@ def entry(out):
 
 
 def generate():
+    """The entry, then per parity of the tile index (which stages hold the
+    operands): the dispatch, the straight body, the general unmasked body,
+    the masked body; the final bodies; the slow paths."""
     out = []
     entry(out)
     slows = []
 
-    def step(parity, nextmask, tag):
+    def stages(parity):
         cur, nxt = (0, 1) if parity == 0 else (1, 0)
         kread, vst = (1, 0) if parity == 0 else (0, 1)
         kload, vload = (0, 1) if parity == 0 else (1, 0)
-        slows.append(iteration(out, tag, cur, nxt, kread, vst, kload, vload, False, nextmask))
-        out.append(f"s_add_u32 s{S_J}, s{S_J}, 1")
-        out.append(f"s_sub_u32 s{S_ITER}, s{S_ITER}, 1")
+        return cur, nxt, kread, vst, kload, vload
 
     for parity, P in ((0, "A"), (1, "B")):
         Q = "B" if P == "A" else "A"
         out.append(f"FA_L{P}_%=:")
-        out.append(f"s_cmp_eq_u32 s{S_ITER}, 0")
+        out.append(f"s_cmp_lt_u32 s{S_J}, s{S_FAST}")
+        out.append(f"s_cbranch_scc0 FA_GEN{P}_%=")
+        out.append(f"FA_BODY{P}_%=:")
+        slows.append(iteration(out, P, *stages(parity), "fast"))
+        out.append(f"s_cbranch_scc1 FA_BODY{Q}_%=")
+        out.append(f"s_branch FA_GEN{Q}_%=")
+        out.append(f"FA_GEN{P}_%=:")
+        out.append(f"s_cmp_eq_u32 s{S_J}, s{S_LAST}")
         out.append(f"s_cbranch_scc1 FA_FIN{P}_%=")
         out.append(f"s_add_u32 s{S_T}, s{S_J}, 1")
         out.append(f"s_cmp_ge_u32 s{S_T}, s{S_FM}")
         out.append(f"s_cbranch_scc1 FA_ITM{P}_%=")
-        step(parity, False, P)
+        out.append(f"FA_GB{P}_%=:")
+        slows.append(iteration(out, "G" + P, *stages(parity), "gen"))
+        out.append(f"s_add_u32 s{S_J}, s{S_J}, 1")
         out.append(f"s_branch FA_L{Q}_%=")
         out.append(f"FA_ITM{P}_%=:")
-        step(parity, True, "M" + P)
+        slows.append(iteration(out, "M" + P, *stages(parity), "masked"))
+        out.append(f"s_add_u32 s{S_J}, s{S_J}, 1")
         out.append(f"s_branch FA_L{Q}_%=")
     for parity, P in ((0, "A"), (1, "B")):
-        cur, nxt = (0, 1) if parity == 0 else (1, 0)
-        kread, vst = (1, 0) if parity == 0 else (0, 1)
-        kload, vload = (0, 1) if parity == 0 else (1, 0)
         out.append(f"FA_FIN{P}_%=:")
-        slows.append(iteration(out, "F" + P, cur, nxt, kread, vst, kload, vload, True))
+        slows.append(iteration(out, "F" + P, *stages(parity), "final"))
         out.append("s_branch FA_DONE_%=")
     for slow_lbl, back_lbl, cur, pcur in slows:
         st = Stream(out)
@@ -736,7 +777,7 @@ def clobbers():
     regs += [f"v{i}" for i in range(TS, TS + 4)]
     regs += [f"v{i}" for i in range(TMP, TMP + NTMP)]
     regs += [f"a{i}" for i in range(KR_BASE, VR_BASE + 4 * VRING)]
-    regs += [f"s{i}" for i in range(S_T, 82)]
+    regs += [f"s{i}" for i in range(S_T, S_T + 9)]
     regs += ["vcc", "scc", "m0", "memory"]
     return regs
 

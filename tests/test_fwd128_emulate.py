@@ -158,6 +158,12 @@ def parse(lines):
 
 
 PROG, LABELS = parse(LINES)
+# body entry points: straight (BODY), general unmasked (GB), masked (ITM), final (FIN)
+BODY_AT = {}
+for _name, _pc in LABELS.items():
+    for _kind in ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"):
+        if _name.startswith(_kind):
+            BODY_AT[_pc] = _kind[3:]
 
 
 def mfma(m, args):
@@ -201,11 +207,14 @@ def lane_bf16(m, tok):
 
 
 SLOW_TAKEN = [0]
+BODIES_RUN = []   # body kinds entered by wave 0, in order
 
 
-def run_wave(m, lds, mem, pc):
+def run_wave(m, lds, mem, pc, wave=0):
     """Execute from pc until a barrier (returns its pc + 1) or the end (None)."""
     while pc < len(PROG):
+        if wave == 0 and pc in BODY_AT:
+            BODIES_RUN.append(BODY_AT[pc])
         op, args, off = PROG[pc]
         pc += 1
         if op in ("s_nop", "s_waitcnt"):
@@ -224,7 +233,7 @@ def run_wave(m, lds, mem, pc):
         elif op.startswith("s_cmp_"):
             a, b = m.sval(args[0]), m.sval(args[1])
             m.scc = int({"s_cmp_eq_u32": a == b, "s_cmp_lg_u32": a != b,
-                         "s_cmp_ge_u32": a >= b}[op])
+                         "s_cmp_ge_u32": a >= b, "s_cmp_lt_u32": a < b}[op])
         elif op == "s_add_u32":
             t = m.sval(args[1]) + m.sval(args[2])
             m.scc = int(t > 0xFFFFFFFF)
@@ -244,8 +253,9 @@ def run_wave(m, lds, mem, pc):
             base = m.s[lo] | (m.s[lo + 1] << 32)
             voff = m.vread_u(args[0])
             for l in range(64):
-                data = mem.read16(base + int(voff[l]))
-                dst = m.m0 + 16 * l
+                # the instruction offset applies to both addresses
+                data = mem.read16(base + int(voff[l]) + off)
+                dst = m.m0 + off + 16 * l
                 assert 0 <= dst and dst + 16 <= lds.size, "LDS write out of range"
                 lds[dst:dst + 16] = data
         elif op == "ds_read_b128":
@@ -387,10 +397,10 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
                 m.v[G.VADDR + 2 * db, lane] = 2 * tr_off(tr_row, sw_lo, db)
                 m.v[G.VADDR + 2 * db + 1, lane] = 2 * tr_off(tr_row + 8, sw_hi, db)
             for i in range(4):
-                p = (4 * i + w) * 64 + lane
+                p = (4 * w + i) * 64 + lane
                 row = p >> 4
                 col = 8 * ((p & 15) ^ tile_swz(row))
-                m.v[G.GOFF + i, lane] = (row * D + col) * 2
+                m.v[G.GOFF + i, lane] = (row * D + col) * 2 - 1024 * i
                 m.v[G.GOFF_TAIL + i, lane] = ((min(tlast * BC + row, N - 1) - tlast * BC) * D
                                               + col) * 2
             for rb in range(2):
@@ -402,20 +412,21 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
         kp, vp = KBASE + 2 * TILE * 2, VBASE + TILE * 2
         m.s[G.S_KPTR], m.s[G.S_KPTR + 1] = kp & 0xFFFFFFFF, kp >> 32
         m.s[G.S_VPTR], m.s[G.S_VPTR + 1] = vp & 0xFFFFFFFF, vp >> 32
-        m.s[G.S_M0K] = 2 * TILE * 2 + w * 1024
-        m.s[G.S_M0V] = w * 1024
+        m.s[G.S_M0K] = 2 * TILE * 2 + w * 4096
+        m.s[G.S_M0V] = w * 4096
         m.s[G.S_C] = int(np.float32(sl2).view(np.uint32))
-        m.s[G.S_ITER] = tend - 1
-        m.s[G.S_NK] = max(0, tend - 2)
-        m.s[G.S_NV] = max(0, tend - 1)
+        tail = ragged and tend == nt
+        m.s[G.S_LAST] = tend - 1
+        m.s[G.S_KEND] = max(0, tend - 2)
+        m.s[G.S_KTAILJ] = nt - 3 if tail and nt >= 3 else 0xFFFFFFFF
+        m.s[G.S_VTAILJ] = nt - 2 if tail and nt >= 2 else 0xFFFFFFFF
         m.s[G.S_FM] = fm
+        m.s[G.S_FAST] = max(0, min(fm - 1, (nt - 1 if tail else tend) - 2))
         m.s[G.S_J] = 0
-        m.s[G.S_TAIL] = 1 if (ragged and tend == nt) else 0
-        m.s[G.S_ONES] = 0x3F803F80
         waves.append([m, 0])
     while True:
-        for wv in waves:
-            wv[1] = run_wave(wv[0], lds, mem, wv[1])
+        for w, wv in enumerate(waves):
+            wv[1] = run_wave(wv[0], lds, mem, wv[1], w)
         done = [wv[1] is None for wv in waves]
         assert all(done) or not any(done), "waves disagree on the barrier count"
         if all(done):
@@ -449,7 +460,36 @@ CASES = [
     (700, 512, True, 1.0),
     (600, 256, False, 3.0),
     (520, 256, True, 3.0),
+    (512, 0, False, 1.0),
+    (130, 0, False, 1.0),
+    (1024, 512, True, 1.0),
 ]
+
+
+def expected_bodies(N, q0, causal):
+    """Which body each tile step should take: straight while the next tile is
+    unmasked and both loads are whole tiles, the masked body when the next
+    tile needs a mask, the general one otherwise, the final one last."""
+    nt = -(-N // BC)
+    qmax = min(q0 + BR, N) - 1
+    tend = min(nt, qmax // BC + 1) if causal else nt
+    ragged = N % BC != 0
+    fm = tend
+    if causal:
+        fm = min(fm, q0 // BC)
+    if ragged:
+        fm = min(fm, nt - 1)
+    out = []
+    for j in range(tend - 1):
+        k_whole = j + 2 < tend and not (ragged and j + 2 == nt - 1)
+        v_whole = not (ragged and j + 1 == nt - 1)
+        if j + 1 >= fm:
+            out.append("ITM")
+        elif k_whole and v_whole:
+            out.append("BODY")
+        else:
+            out.append("GB")
+    return out + ["FIN"]
 
 
 @pytest.mark.parametrize("N,q0,causal,kscale", CASES)
@@ -461,7 +501,9 @@ def test_generated_loop_matches_the_oracle(N, q0, causal, kscale):
         k = bf16_to_f32(bf16_bits(k))
     scale = D ** -0.5
     SLOW_TAKEN[0] = 0
+    BODIES_RUN.clear()
     O, L = emulate_workgroup(q, k, v, N, q0, causal, scale)
+    assert BODIES_RUN == expected_bodies(N, q0, causal), BODIES_RUN
     # keys scaled by 3 from key 192 on lift those tiles' weights far past 2^8
     # above the reference set by tile 0: the exact slow path must run there
     assert (SLOW_TAKEN[0] > 0) == (kscale != 1.0), SLOW_TAKEN[0]

@@ -14,7 +14,11 @@ workgroup's LDS and registers:
     no ring slot is overwritten while a product may still read it, every
     barrier is preceded by vmcnt(0), and the emitted wait states cover the
     matrix/vector hazards;
-  * the loop's load counters never load a tile outside the sequence.
+  * the scalar control flow of the whole statement, executed for many
+    sequence lengths, loads every tile once and in order (whole tiles through
+    the plain offsets, only a partial last tile through the clamped ones),
+    masks exactly the tiles holding an invisible key, and takes the straight
+    body exactly where it applies.
 """
 import importlib.util
 import os
@@ -111,62 +115,93 @@ def kernel_offsets():
     for w in range(4):
         for i in range(4):
             for lane in range(64):
-                p = (4 * i + w) * 64 + lane
+                p = (4 * w + i) * 64 + lane
                 row = p >> 4
-                goff[w, i, lane] = 2 * (row * D + 8 * ((p & 15) ^ tile_swz(row)))
+                goff[w, i, lane] = 2 * (row * D + 8 * ((p & 15) ^ tile_swz(row))) - 1024 * i
     return kaddr, vaddr, goff
 
 
 KADDR, VADDR, GOFF = kernel_offsets()
-M0K = 32768   # LDS byte address of K stage 0 (+ wave * 1024 in s64)
+M0K = 32768   # LDS byte address of K stage 0 (+ wave * 4096 in s64)
 M0V = 0
+NONE = 0xFFFFFFFF
 
 
-def load_path(lines, tail):
-    """The instructions executed by the load blocks when the load is (not) the
-    partial last tile: the tail branch jumps over the plain loads, the plain
-    path jumps over the tail loads."""
-    out, skip_to = [], None
-    for l in lines:
-        if skip_to is not None:
-            if l == skip_to:
-                skip_to = None
-                out.append(l)
+def follow(lines, env):
+    """The lines a body executes for the given scalar registers: compares and
+    branches are evaluated (a branch to a label outside `lines` ends the
+    path); every other line is kept in order."""
+    labels = {l[:-1]: i for i, l in enumerate(lines) if l.endswith(":")}
+    out, pc, scc = [], 0, None
+    while pc < len(lines):
+        l = lines[pc]
+        pc += 1
+        op, args = split(l)
+        if op.startswith("s_cmp_"):
+            x, y = (env[int(t[1:])] if t.startswith("s") else int(t, 0) for t in args[:2])
+            scc = {"s_cmp_eq_u32": x == y, "s_cmp_lg_u32": x != y, "s_cmp_ge_u32": x >= y,
+                   "s_cmp_lt_u32": x < y}[op]
+        elif op in ("s_cbranch_scc0", "s_cbranch_scc1"):
+            assert scc is not None, l
+            if scc == (op == "s_cbranch_scc1"):
+                if args[0] + ":" not in lines:
+                    break
+                pc = labels[args[0]]
             continue
+        elif op == "s_branch":
+            if args[0] + ":" not in lines:
+                break
+            pc = labels[args[0]]
+            continue
+        elif op in ("s_add_u32", "s_addc_u32"):
+            scc = None     # carry, not a comparison
         out.append(l)
-        if tail and l.startswith("s_cbranch_scc1 FA_TAIL"):
-            skip_to = l.split()[1] + ":"
-        elif not tail and l.startswith("s_branch FA_LDONE"):
-            skip_to = l.split()[1] + ":"
     return out
 
 
-def stage_tiles(lines, ktile, vtile, tail=False, offs=None):
+# scalar registers of one step for each load case: tile j = 5; whole loads,
+# the clamped K tile, no K tile, or no K tile and the clamped V tile
+LOAD_CASES = {
+    "whole": {G.S_KEND: 10, G.S_KTAILJ: NONE, G.S_VTAILJ: NONE},
+    "ktail": {G.S_KEND: 10, G.S_KTAILJ: 5, G.S_VTAILJ: NONE},
+    "kskip": {G.S_KEND: 5, G.S_KTAILJ: NONE, G.S_VTAILJ: NONE},
+    "vtail": {G.S_KEND: 5, G.S_KTAILJ: NONE, G.S_VTAILJ: 5},
+}
+
+
+def env_of(case):
+    return {**LOAD_CASES[case], G.S_J: 5, G.S_FAST: 0}
+
+
+def stage_tiles(lines, ktile, vtile, tail_offs=None):
     """Execute the direct loads in `lines` for all four waves into a 64 KiB LDS
-    image (uint16 elements).  Returns the image and which stages were loaded."""
+    image (uint16 elements): whole-tile loads use the kernel's offsets, the
+    clamped ones `tail_offs`; the instruction offset applies to both
+    addresses.  Returns the image and {(K|V, stage, clamped)} loaded."""
     lds = np.full(32768, -1, np.int64)
     loaded = set()
-    offs = GOFF if offs is None else offs
-    lines = load_path(lines, tail)
     for w in range(4):
         m0 = None
         for l in lines:
             op, args = split(l)
             if op == "s_add_u32" and args[0] == "m0":
-                base = {"s64": M0K, "s65": M0V}[args[1]] + 1024 * w
-                m0 = base + int(args[2])
+                m0 = {"s64": M0K, "s65": M0V}[args[1]] + 4096 * w + int(args[2])
             elif op == "global_load_lds_dwordx4":
                 reg = int(args[0][1:])
-                i = reg - (G.GOFF_TAIL if tail else G.GOFF)
+                clamped = reg >= G.GOFF_TAIL
+                i = reg - (G.GOFF_TAIL if clamped else G.GOFF)
                 assert 0 <= i < 4, l
-                tile = ktile if args[1] == f"s[{G.S_KPTR}:{G.S_KPTR + 1}]" else vtile
-                flat = tile.reshape(-1)
+                off = int(args[2].split(":")[1]) if len(args) > 2 else 0
+                offs = tail_offs if clamped else GOFF
+                is_k = args[1] == f"s[{G.S_KPTR}:{G.S_KPTR + 1}]"
+                flat = (ktile if is_k else vtile).reshape(-1)
                 for lane in range(64):
-                    src = offs[w, i, lane] // 2
-                    dst = (m0 + 16 * lane) // 2
+                    src = (offs[w, i, lane] + off) // 2
+                    dst = (m0 + off + 16 * lane) // 2
+                    assert 0 <= src and src + 8 <= flat.size
                     lds[dst:dst + 8] = flat[src:src + 8]
-                loaded.add(("K" if tile is ktile else "V", (m0 - (M0K if tile is ktile else M0V)
-                                                           - 1024 * w) // 16384))
+                base = M0K if is_k else M0V
+                loaded.add(("K" if is_k else "V", (m0 - base - 4096 * w) // 16384, clamped))
     return lds, loaded
 
 
@@ -264,10 +299,16 @@ def run_operand_model(body, kstage, vstage):
 
 
 BODIES = {  # name: (label, K read stage, V read stage, K load stage, V load stage, final)
-    "A": ("FA_LA_%=:", 1, 0, 0, 1, False), "MA": ("FA_ITMA_%=:", 1, 0, 0, 1, False),
-    "B": ("FA_LB_%=:", 0, 1, 1, 0, False), "MB": ("FA_ITMB_%=:", 0, 1, 1, 0, False),
+    "A": ("FA_BODYA_%=:", 1, 0, 0, 1, False), "B": ("FA_BODYB_%=:", 0, 1, 1, 0, False),
+    "GA": ("FA_GBA_%=:", 1, 0, 0, 1, False), "GB": ("FA_GBB_%=:", 0, 1, 1, 0, False),
+    "MA": ("FA_ITMA_%=:", 1, 0, 0, 1, False), "MB": ("FA_ITMB_%=:", 0, 1, 1, 0, False),
     "FA": ("FA_FINA_%=:", 1, 0, 0, 1, True), "FB": ("FA_FINB_%=:", 0, 1, 1, 0, True),
 }
+# the load cases each body can meet: the straight body only whole tiles, the
+# general unmasked one never the clamped V tile (tile j + 1 would be masked)
+BODY_CASES = {"A": ["whole"], "B": ["whole"], "GA": ["whole", "ktail", "kskip"],
+              "GB": ["whole", "ktail", "kskip"], "MA": list(LOAD_CASES), "MB": list(LOAD_CASES),
+              "FA": ["whole"], "FB": ["whole"]}
 
 
 def body_of(name):
@@ -295,36 +336,40 @@ def tail_offsets(N, tlast):
     for w in range(4):
         for i in range(4):
             for lane in range(64):
-                p = (4 * i + w) * 64 + lane
+                p = (4 * w + i) * 64 + lane
                 row = p >> 4
                 col = 8 * ((p & 15) ^ tile_swz(row))
                 out[w, i, lane] = 2 * ((min(tlast * 64 + row, N - 1) - tlast * 64) * D + col)
     return out
 
 
-@pytest.mark.parametrize("name", list(BODIES))
-@pytest.mark.parametrize("tail", [False, True])
-def test_direct_loads_place_tiles_as_the_reads_expect(name, tail):
-    """The emitted loads (M0 values, offset registers) write chunk q of tile
-    row r to slot q ^ swz(r) of the right stage, for all four waves, and
-    cover each stage exactly once; a partial last tile (here 37 rows) goes
-    through the clamped offsets, its missing rows repeating the last one."""
-    _, _, _, kst, vst, _ = BODIES[name]
+@pytest.mark.parametrize("name,case", [(n, c) for n in BODIES for c in BODY_CASES[n]])
+def test_direct_loads_place_tiles_as_the_reads_expect(name, case):
+    """The emitted loads (M0 values, offset registers, instruction offsets)
+    write chunk q of tile row r to slot q ^ swz(r) of the right stage, for
+    all four waves, and cover each loaded stage exactly once; a partial last
+    tile (here 37 rows) goes through the clamped offsets, its missing rows
+    repeating the last one; a tile past the end is not loaded."""
+    _, _, _, kst, vst, final = BODIES[name]
     N, tlast = 3 * 64 + 37, 3
     ktile = np.arange(64 * D).reshape(64, D) + 10 ** 6
     vtile = np.arange(64 * D).reshape(64, D) + 2 * 10 ** 6
-    offs = tail_offsets(N, tlast) if tail else None
-    lds, loaded = stage_tiles(body_of(name), ktile, vtile, tail, offs)
-    assert loaded == {("K", kst), ("V", vst)}
-    for r in range(64):
-        src = min(r, 36) if tail else r
-        for q in range(16):
-            slot = q ^ tile_swz(r)
-            k = (M0K + kst * 16384) // 2 + r * D + 8 * slot
-            v = (M0V + vst * 16384) // 2 + r * D + 8 * slot
-            assert np.array_equal(lds[k:k + 8], ktile[src, 8 * q:8 * q + 8])
-            assert np.array_equal(lds[v:v + 8], vtile[src, 8 * q:8 * q + 8])
-    assert (lds >= 0).sum() == 2 * 64 * D
+    lines = follow(body_of(name), env_of(case))
+    lds, loaded = stage_tiles(lines, ktile, vtile, tail_offsets(N, tlast))
+    want = set() if final else {
+        "whole": {("K", kst, False), ("V", vst, False)},
+        "ktail": {("K", kst, True), ("V", vst, False)},
+        "kskip": {("V", vst, False)},
+        "vtail": {("V", vst, True)}}[case]
+    assert loaded == want
+    for which, stage, clamped in loaded:
+        tile, base = (ktile, M0K) if which == "K" else (vtile, M0V)
+        for r in range(64):
+            src = min(r, 36) if clamped else r
+            for q in range(16):
+                at = (base + stage * 16384) // 2 + r * D + 8 * (q ^ tile_swz(r))
+                assert np.array_equal(lds[at:at + 8], tile[src, 8 * q:8 * q + 8])
+    assert (lds >= 0).sum() == len(loaded) * 64 * D
 
 
 def mask_semantics(lines):
@@ -399,15 +444,15 @@ def classify(op):
 
 def straight_paths():
     """Instruction sequences as executed: the entry (with and without the
-    first tile's mask), each loop body on its fast path and with its slow
-    path spliced in at its branch, each with the normal and the tail loads."""
+    first tile's mask), each loop body for each load case it can meet, on
+    its fast path and with its slow path spliced in at its branch."""
     paths = []
     entry = LINES[:LINES.index("FA_LA_%=:")]
     i, j = entry.index("s_cbranch_scc1 FA_EMASK_%="), entry.index("FA_EMASK_%=:")
     paths += [entry, entry[:i] + entry[j:]]
     for name in BODIES:
-        for tail in (False, True):
-            body = load_path(body_of(name), tail)
+        for case in BODY_CASES[name]:
+            body = follow(body_of(name), env_of(case))
             paths.append(body)
             slow = section(f"FA_SLOW{name}_%=:", "s_branch")
             i = body.index(f"s_cbranch_vccnz FA_SLOW{name}_%=")
@@ -530,17 +575,37 @@ def test_every_barrier_waits_for_the_direct_loads():
     assert not any(x.startswith("global_load_lds") for x in LINES[:first])
 
 
-def test_m0_set_one_state_before_each_direct_load():
-    for i, l in enumerate(LINES):
-        if l.startswith("global_load_lds"):
-            assert LINES[i - 1] == "s_nop 0" and LINES[i - 2].startswith("s_add_u32 m0,")
+@pytest.mark.parametrize("path", range(NPATHS))
+def test_m0_set_at_least_one_state_before_each_direct_load(path):
+    body = straight_paths()[path]
+    last_m0 = None
+    for i, l in enumerate(body):
+        if l.startswith("s_add_u32 m0,"):
+            last_m0 = i
+        elif l.startswith("global_load_lds"):
+            assert last_m0 is not None and i - last_m0 >= 2, (path, i, l)
+
+
+def test_straight_body_keeps_its_branch_condition():
+    """The straight body compares the next tile index with the straight
+    limit early and branches on SCC after its barrier: nothing in between
+    (its slow path included) may write SCC."""
+    for P in "AB":
+        body = section(f"FA_BODY{P}_%=:", "s_cbranch_scc1 FA_BODY")
+        k = body.index(f"s_cmp_lt_u32 s{G.S_J}, s{G.S_FAST}")
+        slow = section(f"FA_SLOW{P}_%=:", "s_branch")
+        for l in body[k + 1:] + slow:
+            op = l.split()[0]
+            assert not op.startswith("s_") or op in (
+                "s_nop", "s_waitcnt", "s_barrier", "s_cbranch_vccnz"), l
 
 
 # ------------------------------------------------------------ tile counts
-def loop_loads(N, q0, causal):
-    """Replay the loop's control flow and load counters with the kernel's
-    start values: which K and V tiles get loaded (and whether through the
-    clamped offsets), which iterations mask their next tile."""
+def run_control(N, q0, causal):
+    """Execute the scalar part of the whole statement with the kernel's
+    start values (no slow path): which K and V tiles get loaded (and whether
+    through the clamped offsets), which tiles get masked, which body each
+    step takes."""
     BC, BR = 64, 256
     nt = -(-N // BC)
     qmax = min(q0 + BR, N) - 1
@@ -552,39 +617,69 @@ def loop_loads(N, q0, causal):
     if ragged:
         fm = min(fm, nt - 1)
     tail = ragged and tend == nt
-    kload = [(0, False)] + ([(1, False)] if tend > 1 else [])   # prologue (C++, clamped itself)
+    kfull = nt - 1 if tail else tend
+    TB = 64 * 256
+    KB, VB = 1 << 40, 2 << 40
+    s = {G.S_LAST: tend - 1, G.S_KEND: max(0, tend - 2),
+         G.S_KTAILJ: nt - 3 if tail and nt >= 3 else NONE,
+         G.S_VTAILJ: nt - 2 if tail and nt >= 2 else NONE,
+         G.S_FM: fm, G.S_FAST: max(0, min(fm - 1, kfull - 2)), G.S_J: 0}
+    ptr = {G.S_KPTR: KB + 2 * TB, G.S_VPTR: VB + TB}
+    kload = [(0, False)] + ([(1, False)] if tend > 1 else [])   # the C++ prologue's
     vload = [(0, False)]
-    iters, nk, nv, j = tend - 1, max(0, tend - 2), max(0, tend - 1), 0
-    kt, vt = 2, 1
-    masked = [0] if fm == 0 else []
+    masked, bodies = [], []
+    labels = {l[:-1]: i for i, l in enumerate(LINES) if l.endswith(":")}
+    pc, scc, steps = 0, None, 0
     while True:
-        last = iters == 0
-        if nk:
-            kload.append((kt, nk == 1 and tail))
-            kt += 1
-            nk -= 1
-        if nv:
-            vload.append((vt, nv == 1 and tail))
-            vt += 1
-            nv -= 1
-        if last:
+        steps += 1
+        assert steps < 10 ** 6
+        l = LINES[pc]
+        pc += 1
+        if l == "FA_DONE_%=:":
             break
-        if j + 1 >= fm:
-            masked.append(j + 1)
-        j += 1
-        iters -= 1
-    return tend, fm, kload, vload, masked
+        for kind in ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"):
+            if l.startswith(kind) and l.endswith(":"):
+                bodies.append(kind[3:])
+                if kind == "FA_ITM":
+                    masked.append(s[G.S_J] + 1)
+        if l == "s_cbranch_scc1 FA_EMASK_%=" and s[G.S_FM] == 0:
+            masked.append(0)
+        op, args = split(l)
+        if op.startswith("s_cmp_"):
+            x, y = (s[int(t[1:])] if t.startswith("s") else int(t, 0) for t in args[:2])
+            scc = {"s_cmp_eq_u32": x == y, "s_cmp_lg_u32": x != y, "s_cmp_ge_u32": x >= y,
+                   "s_cmp_lt_u32": x < y}[op]
+        elif op in ("s_cbranch_scc0", "s_cbranch_scc1"):
+            if scc == (op == "s_cbranch_scc1"):
+                pc = labels[args[0]]
+        elif op == "s_branch":
+            pc = labels[args[0]]
+        elif op == "s_add_u32" and args[0] in (f"s{G.S_KPTR}", f"s{G.S_VPTR}"):
+            ptr[int(args[0][1:])] += int(args[2])
+        elif op == "s_add_u32" and args[0] != "m0":
+            s[int(args[0][1:])] = s[int(args[1][1:])] + int(args[2])
+        elif op == "global_load_lds_dwordx4":
+            reg = int(args[0][1:])
+            if reg in (G.GOFF, G.GOFF_TAIL):
+                p = ptr[int(args[1][2:].split(":")[0])]
+                is_k = p < VB
+                t = (p - (KB if is_k else VB)) // TB
+                assert 0 <= t < nt, (N, q0, t)
+                (kload if is_k else vload).append((t, reg == G.GOFF_TAIL))
+    return tend, fm, kload, vload, masked, bodies
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 200, 256, 300, 511, 512, 700, 1000,
-                               1024, 8192])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 200, 256, 300, 511, 512,
+                               700, 1000, 1024, 8192])
 def test_loop_loads_and_masks(N, causal):
     """Every tile in [0, tend) is loaded once, in order, whole tiles through
     the plain offsets and only a partial last tile through the clamped ones;
-    exactly the tiles that hold an invisible key are masked."""
+    exactly the tiles that hold an invisible key are masked; every step
+    before the last takes the straight body when its next tile is unmasked
+    and both its loads are whole tiles."""
     for q0 in range(0, N, 256):
-        tend, fm, kload, vload, masked = loop_loads(N, q0, causal)
+        tend, fm, kload, vload, masked, bodies = run_control(N, q0, causal)
         assert [t for t, _ in kload] == list(range(tend))
         assert [t for t, _ in vload] == list(range(tend))
         for t, clamped in kload[2:] + vload[1:]:
@@ -592,3 +687,8 @@ def test_loop_loads_and_masks(N, causal):
         need = [t for t in range(tend)
                 if t * 64 + 63 >= N or (causal and t * 64 + 63 > q0)]
         assert masked == need, (N, q0, masked, need)
+        want = []
+        for j in range(tend - 1):
+            whole = j + 2 < tend and (j + 2) * 64 + 63 < N and (j + 1) * 64 + 63 < N
+            want.append("ITM" if j + 1 in need else "BODY" if whole else "GB")
+        assert bodies == want + ["FIN"], (N, q0, bodies, want)
