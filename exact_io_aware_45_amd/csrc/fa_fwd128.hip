@@ -23,6 +23,9 @@
 #include "fa_internal.hpp"
 #include "fa_fwd128_loop.inc"
 
+#include <algorithm>
+#include <atomic>
+
 namespace fa {
 
 namespace {
@@ -38,232 +41,360 @@ constexpr int TILE_BYTES = TILE * 2;
 
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
+// One direct HBM -> LDS load of 16 bytes per lane, issued where the compiler
+// does not track it: lane l's bytes at gbase + voff land at LDS byte address
+// m0 + 16 l.  The caller waits (s_waitcnt vmcnt) and synchronises before any
+// wave reads them, and issues it only once every read of that LDS has
+// returned.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t m0) {
+  const uint64_t g = reinterpret_cast<uint64_t>(gbase);
+  const uint64_t gs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
+  const uint32_t ms = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(ms), "v"(voff), "s"(gs)
+               : "memory", "m0");
+}
+
+// The lane index, recomputed where it is called (the statement is opaque, so
+// nothing derived from it is hoisted across the key loop, which overwrites
+// every vector register).
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Sizes of a launch, re-read in each round of the workgroup's item loop
+// (through `fresh`) so that nothing derived from them is hoisted across the
+// key loop, which overwrites every vector register and most scalar ones.
+struct Shape {
+  int N, H, Hkv, nq, total, nt;
+  bool ragged;
+};
+
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t fresh(uint32_t x) { return (uint32_t)fresh((int)x); }
+__device__ __forceinline__ float fresh(float x) {
+  return __builtin_bit_cast(float, fresh(__builtin_bit_cast(int, x)));
+}
+template <typename T>
+__device__ __forceinline__ T* fresh(T* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  return reinterpret_cast<T*>(((uint64_t)fresh((uint32_t)(x >> 32)) << 32) | fresh((uint32_t)x));
+}
+
+// A query tile of one head: 256 rows from q0 (grid item).
+struct Item {
+  int bh, q0;
+};
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd128_kernel(FwdArgs a) {
-  // LDS: V stage 0, V stage 1, K stage 0, K stage 1 (16 KiB each; the
-  // generated loop addresses this map directly), then the workgroup's 256
-  // query rows as four 64-row tiles (read once into registers).  After the
-  // loop each wave stages its normalised output rows in the first 64 KiB.
-  __shared__ __attribute__((aligned(1024))) bf16 smem[8 * TILE];
-  auto Vst = [&](int stage) { return smem + stage * TILE; };
-  auto Kst = [&](int stage) { return smem + (2 + stage) * TILE; };
-  auto Qst = [&](int i) { return smem + (4 + i) * TILE; };
-  const uint32_t lds0 =
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem));
+  // LDS, bytes: [0, 64K) V stage 0, V stage 1, K stage 0, K stage 1 (the
+  // generated loop addresses these directly); [64K, 128K) each wave's 64
+  // query rows; [128K, 160K) each wave's output staging (32 rows).
+  __shared__ __attribute__((aligned(1024))) bf16 smem[10 * TILE];
+  constexpr uint32_t KST0 = 2 * TILE_BYTES, QST0 = 4 * TILE_BYTES, OST0 = 8 * TILE_BYTES;
+  const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int N = a.N;
-  const int nq = (N + BR - 1) / BR;
-  const int total = nq * a.B * a.H;
-  const int w = xcd_remap(blockIdx.x, total);
-  int bh = w / nq, qt = w % nq;
-  if constexpr (CAUSAL) {
-    int rank;
-    causal_order(w, total, nq, bh, rank);
-    qt = nq - 1 - rank;
-  }
-  const int q0 = qt * BR;
+  auto shape = [&]() {
+    Shape sh;
+    sh.N = fresh(a.N);
+    sh.H = fresh(a.H);
+    sh.Hkv = fresh(a.Hkv);
+    sh.nq = (sh.N + BR - 1) / BR;
+    sh.total = sh.nq * fresh(a.B) * sh.H;
+    sh.nt = (sh.N + BC - 1) / BC;
+    sh.ragged = (sh.N % BC) != 0;
+    return sh;
+  };
+  auto lds_base = [&]() {
+    return fresh(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem)));
+  };
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
+  // The workgroup stays resident and takes items in turn: round r's item is
+  // the one a one-item-per-workgroup launch would give to block b_r, where
+  // b_r walks this workgroup's XCD share (blocks b with b % 8 fixed) in a
+  // serpentine, so that causal items heavy early in one round pair with
+  // light ones in the next.
+  auto item_of = [&](const Shape& sh, int r, Item& it) -> bool {
+    const int G = fresh((int)gridDim.x), g = fresh((int)blockIdx.x);
+    int b;
+    if (G % 8 == 0 && sh.total % 8 == 0) {
+      const int gx = G / 8, x = g % 8, k = g / 8;
+      b = x + 8 * (r * gx + ((r & 1) ? gx - 1 - k : k));
+    } else {
+      b = r * G + ((r & 1) ? G - 1 - g : g);
+    }
+    if (b >= sh.total) return false;
+    const int w = xcd_remap(b, sh.total);
+    int bh = w / sh.nq, qt = w % sh.nq;
+    if constexpr (CAUSAL) {
+      int rank;
+      causal_order(w, sh.total, sh.nq, bh, rank);
+      qt = sh.nq - 1 - rank;
+    }
+    it.bh = __builtin_amdgcn_readfirstlane(bh);
+    it.q0 = __builtin_amdgcn_readfirstlane(qt * BR);
+    return true;
+  };
+  auto kv_off = [&](const Shape& sh, const Item& it) {
+    const int bkv = (it.bh / sh.H) * sh.Hkv + (it.bh % sh.H) / (sh.H / sh.Hkv);
+    return (size_t)bkv * (size_t)sh.N * D;
+  };
+  auto tend_of = [&](const Shape& sh, const Item& it) {
+    return CAUSAL ? min(sh.nt, (min(it.q0 + BR, sh.N) - 1) / BC + 1) : sh.nt;
+  };
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const int bkv = (bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv);
-  const size_t kvhead = (size_t)bkv * (size_t)N * D;
-  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q) + head;
-  const bf16* __restrict__ K = reinterpret_cast<const bf16*>(a.k) + kvhead;
-  const bf16* __restrict__ V = reinterpret_cast<const bf16*>(a.v) + kvhead;
-  bf16* __restrict__ O = reinterpret_cast<bf16*>(a.o) + head;
-
-  const int wrow0 = q0 + 64 * wave;
-
-  // Key tiles [0, tend); from tile fm on every tile needs a mask (the
-  // causal diagonal tiles and a partial last tile).
-  const int nt = (N + BC - 1) / BC;
-  const int qmax = min(q0 + BR, N) - 1;
-  const int tend = CAUSAL ? min(nt, qmax / BC + 1) : nt;
-  const bool ragged = (N % BC) != 0;
-  int fm = tend;
-  if (CAUSAL) fm = min(fm, q0 / BC);
-  if (ragged) fm = min(fm, nt - 1);
-
-  // Direct HBM -> LDS loads of one tile: this wave's i-th load fills LDS
-  // slots p = (4i + wave) * 64 + lane (16 bytes each), row p / 16, slot
-  // p % 16 holding the row's chunk slot ^ swz(row).  Rows past the end of
-  // the sequence repeat the last row (their scores are masked).
-  auto load_tile = [&](const bf16* src, int t, bf16* dst) {
+  // Direct loads of key tile t of `src` into the stage at LDS byte `stage`:
+  // wave w loads rows 16w .. 16w + 15, four rows per load, chunk q of row r
+  // to slot q ^ swz(r); rows past the sequence repeat its last row.
+  auto dma_tile = [&](const Shape& sh, const bf16* src, int t, uint32_t stage) {
+    const int wave = fresh(wave0);
+    const int lane = fresh_lane();
+    const int rows = min(BC, sh.N - t * BC);
+    const uint32_t base = lds_base() + stage + 4096u * wave;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int base = (4 * i + wave) * 64;
-      const int p = base + lane;
-      const int row = p >> 4;
-      const int q = (p & 15) ^ tile_swz<D>(row);
-      lds_load16(src + (size_t)min(t * BC + row, N - 1) * D + 8 * q, dst + 8 * base);
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      const int col = 8 * ((lane & 15) ^ tile_swz<D>(row));
+      dma16(src + (size_t)t * TILE, (uint32_t)(min(row, rows - 1) * D + col) * 2u,
+            base + 1024u * i);
     }
   };
-
-  f32x16 o[2][4];
+  // This wave's 64 query rows of an item into its own Q area (rows past the
+  // sequence repeat its last row; their outputs are never stored).
+  auto dma_q = [&](const Shape& sh, const Item& it) {
+    const bf16* src = fresh(reinterpret_cast<const bf16*>(a.q)) + (size_t)it.bh * (size_t)sh.N * D;
+    const int wave = fresh(wave0);
+    const int lane = fresh_lane();
+    const int r0 = it.q0 + 64 * wave;
+    const uint32_t base = lds_base() + QST0 + 16384u * wave;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.f;
-  const float sl2 = a.scale * kLog2e;
-
-  // Lane parts of the LDS operand addresses (byte addresses of stage 0).
-  const int sw_row = tile_swz<D>(l32);
-  const int tr_row = 4 * h + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
-  const int tq = tr_col >> 3, te = tr_col & 7;
-  auto tr_off = [&](int row, int sw, int b) {
-    return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const int col = 8 * ((lane & 15) ^ tile_swz<D>(row));
+      dma16(src, (uint32_t)(min(r0 + row, sh.N - 1) * D + col) * 2u, base + 1024u * i);
+    }
   };
-  u32x8 kaddr, vaddr;
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    kaddr[c] = lds0 + 2u * (2 * TILE + l32 * D + 8 * ((2 * c + h) ^ sw_row));
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    vaddr[2 * db] = lds0 + 2u * tr_off(tr_row, sw_lo, db);
-    vaddr[2 * db + 1] = lds0 + 2u * tr_off(tr_row + 8, sw_hi, db);
-  }
-  // Direct-load offsets within a tile (wave w loads rows 16w .. 16w + 15,
-  // four rows per load; load i carries instruction offset 1024 i, which
-  // applies to both the global and the LDS address, so it is taken off
-  // here), and for the partial last tile with its rows clamped to the
-  // sequence (absolute: those loads move M0 instead).
-  u32x4 goff, gtail;
-  const int tlast = tend - 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (4 * wave + i) * 64 + lane;
-    const int row = p >> 4;
-    const int col = 8 * ((p & 15) ^ tile_swz<D>(row));
-    goff[i] = (uint32_t)(row * D + col) * 2u - 1024u * i;
-    gtail[i] = (uint32_t)((min(tlast * BC + row, N - 1) - tlast * BC) * D + col) * 2u;
-  }
-  // Mask thresholds for tile fm: a score is masked when its key exceeds the
-  // row's last visible key (the row itself when causal, N - 1 always).
-  float thr[2];
-  int thri[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = wrow0 + 32 * rb + l32;
-    const int lim = CAUSAL ? min(row, N - 1) : N - 1;
-    thri[rb] = lim - 4 * h - BC * fm;
-    thr[rb] = __builtin_bit_cast(float, thri[rb]);
-  }
+  auto dma_first_tiles = [&](const Shape& sh, const Item& it) {
+    const size_t kv = kv_off(sh, it);
+    const bf16* K = fresh(reinterpret_cast<const bf16*>(a.k)) + kv;
+    const bf16* V = fresh(reinterpret_cast<const bf16*>(a.v)) + kv;
+    dma_tile(sh, K, 0, KST0);
+    dma_tile(sh, V, 0, 0);
+    if (tend_of(sh, it) > 1) dma_tile(sh, K, 1, KST0 + TILE_BYTES);
+  };
 
-  // Prologue: the workgroup's query rows, K_0, V_0 and K_1 in flight
-  // together, all by coalesced direct loads into swizzled tiles.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) load_tile(Q, q0 / BC + i, Qst(i));
-  load_tile(K, 0, Kst(0));
-  load_tile(V, 0, Vst(0));
-  if (tend > 1) load_tile(K, 1, Kst(1));
-  wait_global_loads();
+  Item cur;
+  {
+    const Shape sh = shape();
+    if (!item_of(sh, 0, cur)) return;
+    dma_q(sh, cur);
+    dma_first_tiles(sh, cur);
+  }
+  wait_vmem();
   __syncthreads();
 
-  // Q^T operands: row block rb holds query rows q0 + 64 wave + 32 rb + l32,
-  // d = 16c + 8h .. +7 (rows past N - 1 repeat row N - 1; never stored).
-  bf16x8 qf[2][8];
+  for (int r = 0;; ++r) {
+    const Shape sh = shape();
+    const int wave = fresh(wave0);
+    const int N = sh.N, nt = sh.nt;
+    const uint32_t lds0 = lds_base();
+    const int lane = fresh_lane();
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int q0 = cur.q0;
+    const int wrow0 = q0 + 64 * wave;
+    const size_t kv = kv_off(sh, cur);
+    const bf16* __restrict__ K = fresh(reinterpret_cast<const bf16*>(a.k)) + kv;
+    const bf16* __restrict__ V = fresh(reinterpret_cast<const bf16*>(a.v)) + kv;
+
+    // Key tiles [0, tend); from tile fm on every tile needs a mask (the
+    // causal diagonal tiles and a partial last tile).
+    const int tend = tend_of(sh, cur);
+    int fm = tend;
+    if (CAUSAL) fm = min(fm, q0 / BC);
+    if (sh.ragged) fm = min(fm, nt - 1);
+
+    // Q^T operands: row block rb holds query rows q0 + 64 wave + 32 rb + l32,
+    // d = 16c + 8h .. +7.
+    const int sw_row = tile_swz<D>(l32);
+    bf16x8 qf[2][8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        qf[rb][c] = lds_read8(smem + QST0 / 2 + wave * TILE + (32 * rb + l32) * D +
+                              8 * ((2 * c + h) ^ sw_row));
+    // The next item's query rows replace these once they are in registers.
+    Item nxt;
+    const bool more = item_of(sh, r + 1, nxt);
+    if (more) {
+      wait_lds();
+      dma_q(sh, nxt);
+    }
+
+    // Lane parts of the LDS operand addresses (byte addresses of stage 0).
+    const int tr_row = 4 * h + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int sw_lo = tile_swz<D>(tr_row), sw_hi = tile_swz<D>(tr_row + 8);
+    const int tq = tr_col >> 3, te = tr_col & 7;
+    auto tr_off = [&](int row, int sw, int b) {
+      return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te;
+    };
+    u32x8 kaddr, vaddr;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      qf[rb][c] = lds_read8(Qst(wave) + (32 * rb + l32) * D + 8 * ((2 * c + h) ^ sw_row));
-
-  // Scalar operands (wave-uniform values, moved to SGPRs explicitly).
-  auto uni = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); };
-  auto uni64 = [&](uint64_t x) {
-    return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x);
-  };
-  const uint32_t m0k = uni(lds0 + 2 * TILE * 2 + wave * 4096);
-  const uint32_t m0v = uni(lds0 + wave * 4096);
-  const uint32_t cbits = uni(__builtin_bit_cast(uint32_t, sl2));
-  uint64_t kptr = uni64(reinterpret_cast<uint64_t>(K + 2 * (size_t)TILE));
-  uint64_t vptr = uni64(reinterpret_cast<uint64_t>(V + 1 * (size_t)TILE));
-  // Loop control: iteration j processes tile j and loads K_{j+2} and
-  // V_{j+1}; the partial last tile (loaded by iteration nt - 3 for K, nt - 2
-  // for V) goes through the clamped offsets; iterations below `sfast` have
-  // an unmasked next tile and two whole loads.
-  const bool tail = ragged && tend == nt;
-  const int kfull = tail ? nt - 1 : tend;
-  uint32_t jt = 0;
-  const uint32_t slast = uni((uint32_t)(tend - 1));
-  const uint32_t skend = uni((uint32_t)max(0, tend - 2));
-  const uint32_t sktail = uni(tail && nt >= 3 ? (uint32_t)(nt - 3) : ~0u);
-  const uint32_t svtail = uni(tail && nt >= 2 ? (uint32_t)(nt - 2) : ~0u);
-  const uint32_t sfm = uni((uint32_t)fm);
-  const uint32_t sfast = uni((uint32_t)max(0, min(fm - 1, kfull - 2)));
-  const uint32_t bperm = (uint32_t)((lane ^ 32) << 2);
-  const float ninf = -INFINITY;
-  float mneg0, mneg1, l0 = 0.f, l1 = 0.f;
-  asm volatile(FA_FWD128_LOOP_ASM
-               : "+{a[0:15]}"(o[0][0]), "+{a[16:31]}"(o[0][1]), "+{a[32:47]}"(o[0][2]),
-                 "+{a[48:63]}"(o[0][3]), "+{a[64:79]}"(o[1][0]), "+{a[80:95]}"(o[1][1]),
-                 "+{a[96:111]}"(o[1][2]), "+{a[112:127]}"(o[1][3]),
-                 "={v212}"(mneg0), "={v213}"(mneg1), "+{v214}"(l0), "+{v215}"(l1),
-                 "+{v249}"(thr[0]), "+{v250}"(thr[1]),
-                 "+{s[60:61]}"(kptr), "+{s[62:63]}"(vptr), "+{s71}"(jt)
-               : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]),
-                 "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
-                 "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]),
-                 "{a[152:155]}"(qf[0][6]), "{a[156:159]}"(qf[0][7]),
-                 "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]),
-                 "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
-                 "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]),
-                 "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
-                 "{v[192:199]}"(kaddr), "{v[200:207]}"(vaddr), "{v[208:211]}"(goff),
-                 "{v224}"(bperm), "{v251}"(ninf), "{v[252:255]}"(gtail),
-                 "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s67}"(slast), "{s68}"(skend),
-                 "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast)
-               : FA_FWD128_LOOP_CLOBBERS);
-  const float m_ref[2] = {-mneg0, -mneg1};
-  const float lsum[2] = {l0, l1};
-
-  // Epilogue: O = acc / l (bf16), LSE = m + log2(l) in natural units.  The
-  // loop ended with a barrier, so LDS is free: each wave writes its 64 rows
-  // into its own tile with rows padded to 272 bytes (both the 8-byte writes
-  // of 32 rows and the 16-byte reads of 4 whole rows then touch every bank
-  // equally often), and stores whole rows, 1 KiB of consecutive rows per
-  // store instruction.  Lane values are taken afresh from the exec mask (the
-  // loop used every vector register).
-  constexpr int OST = D + 8;
-  const int el = __lane_id(), eh = el >> 5, e32 = el & 31;
-  FA_LDS bf16* ost = (FA_LDS bf16*)(smem + wave * (64 * OST));
+      kaddr[c] = lds0 + 2u * (2 * TILE + l32 * D + 8 * ((2 * c + h) ^ sw_row));
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int qrow = wrow0 + 32 * rb + e32;
-    const float l_tot = lsum[rb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                                 (el ^ 32) << 2, __builtin_bit_cast(int, lsum[rb])));
-    const float inv = __builtin_amdgcn_rcpf(l_tot);
-    if (qrow < N && eh == 0) a.lse[(size_t)bh * N + qrow] = (m_ref[rb] + fast_log2(l_tot)) * kLn2;
-    FA_LDS bf16* orow = ost + (32 * rb + e32) * OST + 4 * eh;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      bf16x4 v4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[rb][c >> 2][4 * (c & 3) + e] * inv);
-      *reinterpret_cast<FA_LDS bf16x4*>(orow + 8 * c) = v4;
+    for (int db = 0; db < 4; ++db) {
+      vaddr[2 * db] = lds0 + 2u * tr_off(tr_row, sw_lo, db);
+      vaddr[2 * db + 1] = lds0 + 2u * tr_off(tr_row + 8, sw_hi, db);
     }
-  }
-  const FA_LDS bf16* src = ost + (el >> 4) * OST + 8 * (el & 15);
-  bf16* dst = O + (size_t)(wrow0 + (el >> 4)) * D + 8 * (el & 15);
-  if (wrow0 + 64 <= N) {
+    // Direct-load offsets within a tile (wave w loads rows 16w .. 16w + 15,
+    // four rows per load; load i carries instruction offset 1024 i, which
+    // applies to both the global and the LDS address, so it is taken off
+    // here), and for the partial last tile with its rows clamped to the
+    // sequence (absolute: those loads move M0 instead).
+    u32x4 goff, gtail;
+    const int tlast = tend - 1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<bf16x8*>(dst + 4 * i * D) = *reinterpret_cast<const FA_LDS bf16x8*>(src + 4 * i * OST);
-  } else {
-    const int rows = N - wrow0;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      const int col = 8 * ((lane & 15) ^ tile_swz<D>(row));
+      goff[i] = (uint32_t)(row * D + col) * 2u - 1024u * i;
+      gtail[i] = (uint32_t)((min(tlast * BC + row, N - 1) - tlast * BC) * D + col) * 2u;
+    }
+    // Mask thresholds for tile fm: a score is masked when its key exceeds the
+    // row's last visible key (the row itself when causal, N - 1 always).
+    float thr[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (4 * i + (el >> 4) < rows)
-        *reinterpret_cast<bf16x8*>(dst + 4 * i * D) = *reinterpret_cast<const FA_LDS bf16x8*>(src + 4 * i * OST);
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = wrow0 + 32 * rb + l32;
+      const int lim = CAUSAL ? min(row, N - 1) : N - 1;
+      thr[rb] = __builtin_bit_cast(float, lim - 4 * h - BC * fm);
+    }
+
+    // Scalar operands (wave-uniform values, moved to SGPRs explicitly).
+    auto uni = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); };
+    auto uni64 = [&](uint64_t x) {
+      return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x);
+    };
+    const uint32_t m0k = uni(lds0 + KST0 + wave * 4096);
+    const uint32_t m0v = uni(lds0 + wave * 4096);
+    uint32_t cbits;   // scale * log2(e), computed on the vector unit, read back explicitly
+    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(cbits) : "v"(fresh(a.scale) * kLog2e));
+    uint64_t kptr = uni64(reinterpret_cast<uint64_t>(K + 2 * (size_t)TILE));
+    uint64_t vptr = uni64(reinterpret_cast<uint64_t>(V + 1 * (size_t)TILE));
+    // Loop control: iteration j processes tile j and loads K_{j+2} and
+    // V_{j+1}; the partial last tile (loaded by iteration nt - 3 for K, nt - 2
+    // for V) goes through the clamped offsets; iterations below `sfast` have
+    // an unmasked next tile and two whole loads.
+    const bool tail = sh.ragged && tend == nt;
+    const int kfull = tail ? nt - 1 : tend;
+    uint32_t jt = 0;
+    const uint32_t slast = uni((uint32_t)(tend - 1));
+    const uint32_t skend = uni((uint32_t)max(0, tend - 2));
+    const uint32_t sktail = uni(tail && nt >= 3 ? (uint32_t)(nt - 3) : ~0u);
+    const uint32_t svtail = uni(tail && nt >= 2 ? (uint32_t)(nt - 2) : ~0u);
+    const uint32_t sfm = uni((uint32_t)fm);
+    const uint32_t sfast = uni((uint32_t)max(0, min(fm - 1, kfull - 2)));
+    const uint32_t bperm = (uint32_t)((lane ^ 32) << 2);
+    const float ninf = -INFINITY;
+    f32x16 o[2][4];
+    float mneg0, mneg1, l0 = 0.f, l1 = 0.f;
+    asm volatile(FA_FWD128_LOOP_ASM
+                 : "={a[0:15]}"(o[0][0]), "={a[16:31]}"(o[0][1]), "={a[32:47]}"(o[0][2]),
+                   "={a[48:63]}"(o[0][3]), "={a[64:79]}"(o[1][0]), "={a[80:95]}"(o[1][1]),
+                   "={a[96:111]}"(o[1][2]), "={a[112:127]}"(o[1][3]),
+                   "={v212}"(mneg0), "={v213}"(mneg1), "+{v214}"(l0), "+{v215}"(l1),
+                   "+{v249}"(thr[0]), "+{v250}"(thr[1]),
+                   "+{s[60:61]}"(kptr), "+{s[62:63]}"(vptr), "+{s71}"(jt)
+                 : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]),
+                   "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
+                   "{a[144:147]}"(qf[0][4]), "{a[148:151]}"(qf[0][5]),
+                   "{a[152:155]}"(qf[0][6]), "{a[156:159]}"(qf[0][7]),
+                   "{a[160:163]}"(qf[1][0]), "{a[164:167]}"(qf[1][1]),
+                   "{a[168:171]}"(qf[1][2]), "{a[172:175]}"(qf[1][3]),
+                   "{a[176:179]}"(qf[1][4]), "{a[180:183]}"(qf[1][5]),
+                   "{a[184:187]}"(qf[1][6]), "{a[188:191]}"(qf[1][7]),
+                   "{v[192:199]}"(kaddr), "{v[200:207]}"(vaddr), "{v[208:211]}"(goff),
+                   "{v224}"(bperm), "{v251}"(ninf), "{v[252:255]}"(gtail),
+                   "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s67}"(slast), "{s68}"(skend),
+                   "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast)
+                 : FA_FWD128_LOOP_CLOBBERS);
+    const float m_ref[2] = {-mneg0, -mneg1};
+    const float lsum[2] = {l0, l1};
+
+    // The loop ended with a barrier: the stages are free for the next item's
+    // first tiles, which land while this item's output is written.
+    const Shape sh2 = shape();
+    if (more) dma_first_tiles(sh2, nxt);
+
+    // Epilogue: O = acc / l (bf16), LSE = m + log2(l) in natural units.  Each
+    // wave passes its rows through its own 8 KiB LDS area, 32 rows at a time
+    // with chunk-swizzled rows (8-byte writes of 32 rows and 16-byte reads of
+    // 4 whole rows both touch every bank equally often), and stores 1 KiB of
+    // consecutive rows per instruction.
+    const int N2 = sh2.N;
+    const int wave2 = fresh(wave0);
+    const int el = fresh_lane(), eh = el >> 5, e32 = el & 31;
+    FA_LDS char* ost = (FA_LDS char*)smem + OST0 + 8192 * wave2;
+    const int wsw = tile_swz<D>(e32);
+    const int rsub = el >> 4, rch = el & 15;
+    const size_t ohead = (size_t)cur.bh * (size_t)N2;
+    const int wrow2 = cur.q0 + 64 * wave2;
+    typedef __attribute__((address_space(1))) bf16x8 gbf16x8;
+    typedef __attribute__((address_space(1))) float gfloat;
+    gbf16x8* orow0 = (gbf16x8*)(fresh(reinterpret_cast<bf16*>(a.o)) + (ohead + wrow2 + rsub) * D +
+                                8 * rch);
+    gfloat* lse = (gfloat*)(fresh(a.lse) + ohead);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int qrow = wrow2 + 32 * rb + e32;
+      const float l_tot = lsum[rb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                                   (el ^ 32) << 2, __builtin_bit_cast(int, lsum[rb])));
+      const float inv = __builtin_amdgcn_rcpf(l_tot);
+      if (qrow < N2 && eh == 0) lse[qrow] = (m_ref[rb] + fast_log2(l_tot)) * kLn2;
+      FA_LDS char* wrow = ost + 256 * e32 + 8 * eh;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[rb][c >> 2][4 * (c & 3) + e] * inv);
+        *reinterpret_cast<FA_LDS bf16x4*>(wrow + 16 * (c ^ wsw)) = v4;
+      }
+      bf16x8 v8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + rsub;
+        v8[i] = *reinterpret_cast<const FA_LDS bf16x8*>(ost + 256 * row + 16 * (rch ^ tile_swz<D>(row)));
+      }
+      // 1 KiB row groups: orow0 steps by 4 rows (64 of its elements) per i
+      const int rows = N2 - (wrow2 + 32 * rb);
+      if (rows >= 32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) orow0[(32 * rb + 4 * i) * (D / 8)] = v8[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (4 * i + rsub < rows) orow0[(32 * rb + 4 * i) * (D / 8)] = v8[i];
+      }
+    }
+    if (!more) break;
+    wait_vmem();
+    __syncthreads();
+    cur = nxt;
   }
 }
 
@@ -278,9 +409,24 @@ bool fwd128_applies(const FwdArgs& a) {
   return grid >= 256;
 }
 
+// Resident workgroups: one per CU (each takes a whole CU's registers).
+static int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_fwd128(const FwdArgs& a, hipStream_t s) {
-  const long long grid = (long long)((a.N + BR - 1) / BR) * a.B * a.H;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long items = (long long)((a.N + BR - 1) / BR) * a.B * a.H;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long grid = std::min<long long>(items, cu_count());
   if (a.causal)
     hipLaunchKernelGGL((fwd128_kernel<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
   else

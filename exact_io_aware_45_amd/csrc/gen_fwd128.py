@@ -100,7 +100,7 @@ TILE_BYTES = 64 * 256   # one 64-key tile of K or V in global memory
 THRESH = "0x43800000"   # 256.0: the per-lane tile sum that sends a tile to the slow path
 
 # Conservative issue-cycle costs used to fill the shadow of each product.
-COST = {"valu": 4.5, "trans": 8.0, "lds": 4.0, "salu": 4.0, "vmem": 4.0, "nop": 1.0}
+COST = {"valu": 4.5, "trans": 8.0, "accw": 4.5, "lds": 4.0, "salu": 4.0, "vmem": 4.0, "nop": 1.0}
 SLOT = 27.0   # vector/LDS issue cycles one wave can overlap with one product
 
 # Hazard distances (in issued instructions; s_nop N counts N+1).
@@ -668,9 +668,10 @@ def iteration(out, name, cur, nxt, kstage_read, vstage, kstage_load, vstage_load
 
 
 def entry(out):
-    """Scores of tile 0 into buffer 0 (K stage 0), their mask when tile 0
-    needs one, the exact row maxima as the first reference, and tile 0's
-    first-half weights."""
+    """Scores of tile 0 into buffer 0 (K stage 0) with the output
+    accumulators cleared beside them, their mask when tile 0 needs one, the
+    exact row maxima as the first reference, and tile 0's first-half
+    weights."""
     st = Stream(out)
     st.raw("s_nop 4")
     lds = LdsCounter()
@@ -682,7 +683,9 @@ def entry(out):
         need[m] = {("K", o), ("K", o + 1)} if o % 2 == 0 else {("K", o)}
     for o in range(KAHEAD, 16):
         sched.setdefault(2 * (o - KAHEAD), []).append((("K", o), k_read(o, 0)))
-    interleave(st, mf, before, [], lds, sched, need)
+    zero = [Ins(f"v_accvgpr_write_b32 {a(O_BASE + i)}, 0", "accw", [a(O_BASE + i)])
+            for i in range(128)]
+    interleave(st, mf, before, zero, lds, sched, need)
     # every wave has read K_0 before iteration 0 loads K_2 into its stage
     st.raw("s_waitcnt lgkmcnt(0)")
     st.raw("s_barrier")
