@@ -89,8 +89,16 @@ def traffic_bytes(w, which: str) -> float:
 
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd.hip", "fa_common.hpp"),
+    "fwd128_kernel": ("fa_fwd128.hip", "fa_fwd128_loop.inc", "fa_common.hpp"),
     "fa_backward": ("fa_bwd.hip", "fa_common.hpp"),
 }
+
+
+def uses_fwd128(w) -> bool:
+    """Whether fa_forward takes the hand-scheduled d = 128 kernel: bf16, no
+    tile mask, at least 256 query tiles of 256 rows."""
+    return (w.dtype == "bf16" and w.d == 128 and not w.sparse
+            and -(-w.N // 256) * w.B * w.H >= 256)
 
 
 def source_sha(files) -> str:
@@ -434,6 +442,10 @@ def main():
     elif w.dtype == "fp8":
         fwd_kernel = (f"fwd_fp8_kernel<d={w.d}, BC=64, {8 if w.d == 128 else 4} waves, {mode}> "
                       "(1 launch per fa_forward_fp8)")
+    elif uses_fwd128(w):
+        entry = "_gqa" if w.Hkv else ""
+        fwd_kernel = (f"fwd128_kernel<{mode}> (1 launch per fa_forward{entry}; one resident "
+                      "4-wave workgroup per CU, 256-row query tiles)")
     else:
         entry = "_blocksparse" if w.sparse else ("_gqa" if w.Hkv else "")
         fwd_kernel = (f"fwd_bf16_kernel<d={w.d}, BC=64, {nw} waves, {mode}> "
@@ -461,7 +473,9 @@ def main():
         "frac_of_peak": round(value / peak, 4),
         "fwd": {"ms": round(fwd_ms, 4), **spread(fwd_each), "tflops": round(fwd_tf, 2),
                 "frac_of_peak": round(fwd_tf / peak, 4), "flops": ff},
-        "roofline": roofline(w, "fwd", fwd_ms, ff, traffic.get("fwd_bf16_kernel"), fwd_kernel),
+        "roofline": roofline(w, "fwd", fwd_ms, ff,
+                             traffic.get("fwd128_kernel" if uses_fwd128(w) else "fwd_bf16_kernel"),
+                             fwd_kernel),
     }
     if w.Hkv:
         line["config"]["Hkv"] = w.Hkv
