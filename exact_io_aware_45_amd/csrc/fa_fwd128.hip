@@ -202,8 +202,7 @@ void fwd128_kernel(FwdArgs a) {
     dma_q(sh, cur);
     dma_first_tiles(sh, cur);
   }
-  wait_vmem();
-  __syncthreads();
+  wait_vmem();   // each wave reads only its own query rows before the next barrier
 
   for (int r = 0;; ++r) {
     const Shape sh = shape();
@@ -236,13 +235,8 @@ void fwd128_kernel(FwdArgs a) {
       for (int c = 0; c < 8; ++c)
         qf[rb][c] = lds_read8(smem + QST0 / 2 + wave * TILE + (32 * rb + l32) * D +
                               8 * ((2 * c + h) ^ sw_row));
-    // The next item's query rows replace these once they are in registers.
     Item nxt;
     const bool more = item_of(sh, r + 1, nxt);
-    if (more) {
-      wait_lds();
-      dma_q(sh, nxt);
-    }
 
     // Lane parts of the LDS operand addresses (byte addresses of stage 0).
     const int tr_row = 4 * h + ((lane & 15) >> 2);
@@ -311,6 +305,16 @@ void fwd128_kernel(FwdArgs a) {
     const uint32_t sfast = uni((uint32_t)max(0, min(fm - 1, kfull - 2)));
     const uint32_t bperm = (uint32_t)((lane ^ 32) << 2);
     const float ninf = -INFINITY;
+    // This item's first K and V tiles (loaded while the previous output was
+    // written) and that output's stores complete here, after the set-up
+    // above; then the next item's query rows replace this one's, which are
+    // in registers by now.
+    wait_vmem();
+    __syncthreads();
+    if (more) {
+      wait_lds();
+      dma_q(sh, nxt);
+    }
     f32x16 o[2][4];
     float mneg0, mneg1, l0 = 0.f, l1 = 0.f;
     asm volatile(FA_FWD128_LOOP_ASM
@@ -392,8 +396,6 @@ void fwd128_kernel(FwdArgs a) {
       }
     }
     if (!more) break;
-    wait_vmem();
-    __syncthreads();
     cur = nxt;
   }
 }
