@@ -953,6 +953,13 @@ hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
     if (g3 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_dkv_reduce_kernel, dim3((unsigned)g3), dim3(256), 0, s, a, n4);
   }
+  if constexpr (D == 128 && !(MODE & kSparse)) {
+    if (dq128_applies(a)) {   // the hand-scheduled resident kernel (fa_bwd_dq128.hip)
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_dq128(a, s);
+    }
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3((unsigned)g2), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -22,9 +22,9 @@
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 #include "fa_fwd128_loop.inc"
+#include "fa_resident.hpp"
 
 #include <algorithm>
-#include <atomic>
 
 namespace fa {
 
@@ -41,61 +41,6 @@ constexpr int TILE_BYTES = TILE * 2;
 
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
-// One direct HBM -> LDS load of 16 bytes per lane, issued where the compiler
-// does not track it: lane l's bytes at gbase + voff land at LDS byte address
-// m0 + 16 l.  The caller waits (s_waitcnt vmcnt) and synchronises before any
-// wave reads them, and issues it only once every read of that LDS has
-// returned.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t m0) {
-  const uint64_t g = reinterpret_cast<uint64_t>(gbase);
-  const uint64_t gs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
-  const uint32_t ms = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(ms), "v"(voff), "s"(gs)
-               : "memory", "m0");
-}
-
-// The lane index, recomputed where it is called (the statement is opaque, so
-// nothing derived from it is hoisted across the key loop, which overwrites
-// every vector register).
-__device__ __forceinline__ int fresh_lane() {
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Sizes of a launch, re-read in each round of the workgroup's item loop
-// (through `fresh`) so that nothing derived from them is hoisted across the
-// key loop, which overwrites every vector register and most scalar ones.
-struct Shape {
-  int N, H, Hkv, nq, total, nt;
-  bool ragged;
-};
-
-__device__ __forceinline__ int fresh(int x) {
-  asm volatile("" : "+s"(x));
-  return x;
-}
-__device__ __forceinline__ uint32_t fresh(uint32_t x) { return (uint32_t)fresh((int)x); }
-__device__ __forceinline__ float fresh(float x) {
-  return __builtin_bit_cast(float, fresh(__builtin_bit_cast(int, x)));
-}
-template <typename T>
-__device__ __forceinline__ T* fresh(T* p) {
-  const uint64_t x = reinterpret_cast<uint64_t>(p);
-  return reinterpret_cast<T*>(((uint64_t)fresh((uint32_t)(x >> 32)) << 32) | fresh((uint32_t)x));
-}
-
-// A query tile of one head: 256 rows from q0 (grid item).
-struct Item {
-  int bh, q0;
-};
-
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd128_kernel(FwdArgs a) {
@@ -106,85 +51,28 @@ void fwd128_kernel(FwdArgs a) {
   constexpr uint32_t KST0 = 2 * TILE_BYTES, QST0 = 4 * TILE_BYTES, OST0 = 8 * TILE_BYTES;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  auto shape = [&]() {
-    Shape sh;
-    sh.N = fresh(a.N);
-    sh.H = fresh(a.H);
-    sh.Hkv = fresh(a.Hkv);
-    sh.nq = (sh.N + BR - 1) / BR;
-    sh.total = sh.nq * fresh(a.B) * sh.H;
-    sh.nt = (sh.N + BC - 1) / BC;
-    sh.ragged = (sh.N % BC) != 0;
-    return sh;
-  };
+  auto shape = [&]() { return fresh_shape<BR, BC>(a.N, a.B, a.H, a.Hkv); };
   auto lds_base = [&]() {
     return fresh(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem)));
   };
 
-  // The workgroup stays resident and takes items in turn: round r's item is
-  // the one a one-item-per-workgroup launch would give to block b_r, where
-  // b_r walks this workgroup's XCD share (blocks b with b % 8 fixed) in a
-  // serpentine, so that causal items heavy early in one round pair with
-  // light ones in the next.
-  auto item_of = [&](const Shape& sh, int r, Item& it) -> bool {
-    const int G = fresh((int)gridDim.x), g = fresh((int)blockIdx.x);
-    int b;
-    if (G % 8 == 0 && sh.total % 8 == 0) {
-      const int gx = G / 8, x = g % 8, k = g / 8;
-      b = x + 8 * (r * gx + ((r & 1) ? gx - 1 - k : k));
-    } else {
-      b = r * G + ((r & 1) ? G - 1 - g : g);
-    }
-    if (b >= sh.total) return false;
-    const int w = xcd_remap(b, sh.total);
-    int bh = w / sh.nq, qt = w % sh.nq;
-    if constexpr (CAUSAL) {
-      int rank;
-      causal_order(w, sh.total, sh.nq, bh, rank);
-      qt = sh.nq - 1 - rank;
-    }
-    it.bh = __builtin_amdgcn_readfirstlane(bh);
-    it.q0 = __builtin_amdgcn_readfirstlane(qt * BR);
-    return true;
+  auto item_of = [&](const Shape& sh, int r, Item& it) {
+    return resident_item<CAUSAL, BR>(sh, r, it);
   };
-  auto kv_off = [&](const Shape& sh, const Item& it) {
-    const int bkv = (it.bh / sh.H) * sh.Hkv + (it.bh % sh.H) / (sh.H / sh.Hkv);
-    return (size_t)bkv * (size_t)sh.N * D;
-  };
+  auto kv_off = [&](const Shape& sh, const Item& it) { return kv_head_offset(sh, it.bh, D); };
   auto tend_of = [&](const Shape& sh, const Item& it) {
     return CAUSAL ? min(sh.nt, (min(it.q0 + BR, sh.N) - 1) / BC + 1) : sh.nt;
   };
 
-  // Direct loads of key tile t of `src` into the stage at LDS byte `stage`:
-  // wave w loads rows 16w .. 16w + 15, four rows per load, chunk q of row r
-  // to slot q ^ swz(r); rows past the sequence repeat its last row.
   auto dma_tile = [&](const Shape& sh, const bf16* src, int t, uint32_t stage) {
-    const int wave = fresh(wave0);
-    const int lane = fresh_lane();
-    const int rows = min(BC, sh.N - t * BC);
-    const uint32_t base = lds_base() + stage + 4096u * wave;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wave + 4 * i + (lane >> 4);
-      const int col = 8 * ((lane & 15) ^ tile_swz<D>(row));
-      dma16(src + (size_t)t * TILE, (uint32_t)(min(row, rows - 1) * D + col) * 2u,
-            base + 1024u * i);
-    }
+    dma_tile128(sh, fresh(wave0), src, t, lds_base() + stage);
   };
-  // This wave's 64 query rows of an item into its own Q area (rows past the
-  // sequence repeat its last row; their outputs are never stored).
+  // This wave's 64 query rows of an item into its own Q area (their outputs
+  // are stored only for rows inside the sequence).
   auto dma_q = [&](const Shape& sh, const Item& it) {
-    const bf16* src = fresh(reinterpret_cast<const bf16*>(a.q)) + (size_t)it.bh * (size_t)sh.N * D;
     const int wave = fresh(wave0);
-    const int lane = fresh_lane();
-    const int r0 = it.q0 + 64 * wave;
-    const uint32_t base = lds_base() + QST0 + 16384u * wave;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 4 * i + (lane >> 4);
-      const int col = 8 * ((lane & 15) ^ tile_swz<D>(row));
-      dma16(src, (uint32_t)(min(r0 + row, sh.N - 1) * D + col) * 2u, base + 1024u * i);
-    }
+    dma_rows128(sh, fresh(reinterpret_cast<const bf16*>(a.q)) + (size_t)it.bh * (size_t)sh.N * D,
+                it.q0 + 64 * wave, lds_base() + QST0 + 16384u * wave);
   };
   auto dma_first_tiles = [&](const Shape& sh, const Item& it) {
     const size_t kv = kv_off(sh, it);
@@ -411,24 +299,10 @@ bool fwd128_applies(const FwdArgs& a) {
   return grid >= 256;
 }
 
-// Resident workgroups: one per CU (each takes a whole CU's registers).
-static int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 hipError_t launch_fwd128(const FwdArgs& a, hipStream_t s) {
   const long long items = (long long)((a.N + BR - 1) / BR) * a.B * a.H;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const long long grid = std::min<long long>(items, cu_count());
+  const long long grid = std::min<long long>(items, resident_cu_count());
   if (a.causal)
     hipLaunchKernelGGL((fwd128_kernel<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
   else

@@ -58,5 +58,7 @@ hipError_t launch_fwd128(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+bool dq128_applies(const BwdArgs& a);
+hipError_t launch_dq128(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -1,24 +1,15 @@
 """CPU emulation of the generated key loop of the d = 128 forward kernel.
 
 The instruction text that gen_fwd128.py emits (fa_fwd128_loop.inc) is
-executed for the four waves of one workgroup on a model of their registers,
-the workgroup's LDS and the global K/V buffers:
-  * scalar and vector instructions with their ISA semantics (fp32 vector
-    arithmetic in float32, bf16 packing by round-to-nearest-even);
-  * v_mfma_f32_32x32x16_bf16 with the operand and accumulator layouts
-    measured on the device (fa_common.hpp);
-  * ds_read_b128 / ds_read_b64_tr_b16 / ds_bpermute_b32 and the direct
-    HBM -> LDS loads (global_load_lds_dwordx4 with M0);
-  * s_barrier: every wave runs up to its next barrier before any goes on.
-Every global load is checked to lie inside the K or V buffer.  The setup
-(registers and the three tiles staged before the loop) restates the C++ of
+executed for the four waves of one workgroup by the emulator in _emu.py
+(registers, LDS, bounds-checked K/V buffers, barriers).  The setup (registers
+and the three tiles staged before the loop) restates the C++ of
 fa_fwd128.hip.  The output is normalised as the kernel's epilogue does and
 compared with the fp64 oracle at the bf16 tolerances.  Hazards and timing
 are not modelled (test_fwd128_schedule.py checks those on the text).
 """
 import importlib.util
 import os
-import re
 
 import numpy as np
 import pytest
@@ -26,6 +17,7 @@ import torch
 
 import oracle
 from exact_io_aware_45_amd import inputs
+from _emu import Machine, Memory, Program, bf16_bits, bf16_to_f32, tile_swz
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEN = os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", "gen_fwd128.py")
@@ -36,302 +28,7 @@ LINES = G.generate()
 D, BC, BR = 128, 64, 256
 
 
-def tile_swz(r):
-    return 4 * (r & 3) + ((r >> 2) & 3)
-
-
-def bf16_bits(x):
-    """float32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
-    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
-    nan = np.isnan(np.asarray(x, np.float32))
-    r[nan] = 0x7FC0
-    return r.astype(np.uint32)
-
-
-def bf16_to_f32(b):
-    return (np.asarray(b, np.uint32) << 16).view(np.float32)
-
-
-REG = re.compile(r"^(-?)([vas])(?:\[(\d+):(\d+)\]|(\d+))$")
-
-
-class Machine:
-    """Registers of one wave."""
-
-    def __init__(self):
-        self.v = np.zeros((256, 64), np.uint32)
-        self.a = np.zeros((256, 64), np.uint32)
-        self.s = [0] * 106
-        self.vcc = np.zeros(64, bool)
-        self.scc = 0
-        self.m0 = 0
-
-    # operand access -------------------------------------------------------
-    def rng(self, tok):
-        m = REG.match(tok)
-        neg, kind = m.group(1) == "-", m.group(2)
-        lo = int(m.group(3) if m.group(3) is not None else m.group(5))
-        hi = int(m.group(4)) if m.group(4) is not None else lo
-        return neg, kind, lo, hi
-
-    def vread(self, tok):
-        """A 32-bit vector operand as float32 per lane (SGPRs broadcast,
-        literals and inline constants accepted)."""
-        if REG.match(tok):
-            neg, kind, lo, _ = self.rng(tok)
-            if kind == "v":
-                x = self.v[lo].view(np.float32).copy()
-            elif kind == "a":
-                x = self.a[lo].view(np.float32).copy()
-            else:
-                x = np.full(64, np.uint32(self.s[lo]), np.uint32).view(np.float32).copy()
-            return -x if neg else x
-        if tok.startswith("0x"):
-            return np.full(64, np.uint32(int(tok, 16)), np.uint32).view(np.float32).copy()
-        return np.full(64, float(tok), np.float32)
-
-    def vread_u(self, tok):
-        if REG.match(tok):
-            _, kind, lo, _ = self.rng(tok)
-            src = {"v": self.v, "a": self.a}[kind] if kind != "s" else None
-            if src is None:
-                return np.full(64, np.uint32(self.s[lo]), np.uint32)
-            return src[lo].copy()
-        return np.full(64, np.uint32(int(tok, 0) & 0xFFFFFFFF), np.uint32)
-
-    def vwrite(self, tok, x):
-        _, kind, lo, _ = self.rng(tok)
-        arr = self.v if kind == "v" else self.a
-        arr[lo] = np.asarray(x).astype(np.float32).view(np.uint32) \
-            if np.asarray(x).dtype != np.uint32 else x
-
-    def block(self, tok):
-        _, kind, lo, hi = self.rng(tok)
-        arr = self.v if kind == "v" else self.a
-        return arr, lo, hi
-
-    def sval(self, tok):
-        if tok == "m0":
-            return self.m0
-        m = REG.match(tok)
-        if m and m.group(2) == "s":
-            return self.s[int(m.group(5))]
-        return int(tok, 0) & 0xFFFFFFFF
-
-    def swrite(self, tok, x):
-        x &= 0xFFFFFFFF
-        if tok == "m0":
-            self.m0 = x
-        else:
-            self.s[int(REG.match(tok).group(5))] = x
-
-
-class Memory:
-    """Global buffers (K, V) at fake addresses; every access is bounds-checked."""
-
-    def __init__(self, bufs):
-        self.bufs = bufs   # list of (base address, uint8 array)
-
-    def read16(self, addr):
-        for base, arr in self.bufs:
-            if base <= addr and addr + 16 <= base + arr.size:
-                return arr[addr - base: addr - base + 16]
-        raise AssertionError(f"global load outside the K/V buffers at {addr:#x}")
-
-
-def parse(lines):
-    prog, labels = [], {}
-    for l in lines:
-        if l.endswith(":"):
-            labels[l[:-1]] = len(prog)
-            continue
-        op, _, rest = l.partition(" ")
-        args = [x.strip() for x in rest.split(",")] if rest else []
-        off = 0
-        if args and " offset:" in args[-1]:
-            reg, _, o = args[-1].partition(" offset:")
-            args[-1] = reg.strip()
-            off = int(o)
-        prog.append((op, args, off))
-    return prog, labels
-
-
-PROG, LABELS = parse(LINES)
-# body entry points: straight (BODY), general unmasked (GB), masked (ITM), final (FIN)
-BODY_AT = {}
-for _name, _pc in LABELS.items():
-    for _kind in ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"):
-        if _name.startswith(_kind):
-            BODY_AT[_pc] = _kind[3:]
-
-
-def mfma(m, args):
-    A = lane_bf16(m, args[1])
-    B = lane_bf16(m, args[2])
-    Amat = np.zeros((32, 16))
-    Bmat = np.zeros((16, 32))
-    for l in range(64):
-        h, i = l >> 5, l & 31
-        Amat[i, 8 * h:8 * h + 8] = A[l]
-        Bmat[8 * h:8 * h + 8, i] = B[l]
-    arr, lo, hi = m.block(args[0])
-    if args[3] == "0":
-        C = np.zeros((16, 64), np.float32)
-    else:
-        carr, clo, _ = m.block(args[3])
-        C = carr[clo:clo + 16].view(np.float32).copy()
-    Cmat = np.zeros((32, 32))
-    for l in range(64):
-        h, j = l >> 5, l & 31
-        for r in range(16):
-            Cmat[8 * (r // 4) + 4 * h + r % 4, j] = C[r, l]
-    Dm = Amat @ Bmat + Cmat
-    out = np.zeros((16, 64), np.float32)
-    for l in range(64):
-        h, j = l >> 5, l & 31
-        for r in range(16):
-            out[r, l] = Dm[8 * (r // 4) + 4 * h + r % 4, j]
-    arr[lo:lo + 16] = out.view(np.uint32)
-
-
-def lane_bf16(m, tok):
-    """8 bf16 per lane from a 4-register operand."""
-    arr, lo, _ = m.block(tok)
-    w = arr[lo:lo + 4]                       # 4 x 64 dwords
-    out = np.zeros((64, 8))
-    for t in range(4):
-        out[:, 2 * t] = bf16_to_f32(w[t] & 0xFFFF)
-        out[:, 2 * t + 1] = bf16_to_f32(w[t] >> 16)
-    return out
-
-
-SLOW_TAKEN = [0]
-BODIES_RUN = []   # body kinds entered by wave 0, in order
-
-
-def run_wave(m, lds, mem, pc, wave=0):
-    """Execute from pc until a barrier (returns its pc + 1) or the end (None)."""
-    while pc < len(PROG):
-        if wave == 0 and pc in BODY_AT:
-            BODIES_RUN.append(BODY_AT[pc])
-        op, args, off = PROG[pc]
-        pc += 1
-        if op in ("s_nop", "s_waitcnt"):
-            continue
-        if op == "s_barrier":
-            return pc
-        if op == "s_branch":
-            pc = LABELS[args[0]]
-        elif op in ("s_cbranch_scc1", "s_cbranch_scc0", "s_cbranch_vccnz"):
-            take = {"s_cbranch_scc1": m.scc == 1, "s_cbranch_scc0": m.scc == 0,
-                    "s_cbranch_vccnz": bool(m.vcc.any())}[op]
-            if take:
-                pc = LABELS[args[0]]
-                if args[0].startswith("FA_SLOW"):
-                    SLOW_TAKEN[0] += 1
-        elif op.startswith("s_cmp_"):
-            a, b = m.sval(args[0]), m.sval(args[1])
-            m.scc = int({"s_cmp_eq_u32": a == b, "s_cmp_lg_u32": a != b,
-                         "s_cmp_ge_u32": a >= b, "s_cmp_lt_u32": a < b}[op])
-        elif op == "s_add_u32":
-            t = m.sval(args[1]) + m.sval(args[2])
-            m.scc = int(t > 0xFFFFFFFF)
-            m.swrite(args[0], t)
-        elif op == "s_addc_u32":
-            t = m.sval(args[1]) + m.sval(args[2]) + m.scc
-            m.scc = int(t > 0xFFFFFFFF)
-            m.swrite(args[0], t)
-        elif op == "s_sub_u32":
-            a, b = m.sval(args[1]), m.sval(args[2])
-            m.scc = int(b > a)
-            m.swrite(args[0], a - b)
-        elif op == "s_cselect_b32":
-            m.swrite(args[0], m.sval(args[1]) if m.scc else m.sval(args[2]))
-        elif op == "global_load_lds_dwordx4":
-            lo = int(REG.match(args[1]).group(3))
-            base = m.s[lo] | (m.s[lo + 1] << 32)
-            voff = m.vread_u(args[0])
-            for l in range(64):
-                # the instruction offset applies to both addresses
-                data = mem.read16(base + int(voff[l]) + off)
-                dst = m.m0 + off + 16 * l
-                assert 0 <= dst and dst + 16 <= lds.size, "LDS write out of range"
-                lds[dst:dst + 16] = data
-        elif op == "ds_read_b128":
-            arr, lo, _ = m.block(args[0])
-            addr = m.vread_u(args[1]) + off
-            for l in range(64):
-                a0 = int(addr[l])
-                assert 0 <= a0 and a0 + 16 <= lds.size, "LDS read out of range"
-                arr[lo:lo + 4, l] = lds[a0:a0 + 16].view(np.uint32)
-        elif op == "ds_read_b64_tr_b16":
-            arr, lo, _ = m.block(args[0])
-            addr = m.vread_u(args[1]) + off
-            res = np.zeros((64, 4), np.uint16)
-            for l in range(64):
-                g, i = l // 16, l % 16
-                for t in range(4):
-                    src = int(addr[16 * g + 4 * t + i // 4])
-                    res[l, t] = lds[src + 2 * (i % 4): src + 2 * (i % 4) + 2].view(np.uint16)[0]
-            arr[lo:lo + 2] = res.view(np.uint32).T
-        elif op == "ds_bpermute_b32":
-            addr = m.vread_u(args[1])
-            src = m.vread_u(args[2])
-            m.vwrite(args[0], src[(addr // 4) % 64])
-        elif op == "v_mfma_f32_32x32x16_bf16":
-            mfma(m, args)
-        elif op == "v_fma_f32":
-            x = np.float32(1) * (m.vread(args[1]).astype(np.float64) * m.vread(args[2])
-                                 + m.vread(args[3]))
-            m.vwrite(args[0], x.astype(np.float32))
-        elif op in ("v_exp_f32", "v_exp_f32_e64"):
-            with np.errstate(over="ignore"):
-                m.vwrite(args[0], np.exp2(m.vread(args[1])).astype(np.float32))
-        elif op == "v_add_f32":
-            m.vwrite(args[0], m.vread(args[1]) + m.vread(args[2]))
-        elif op == "v_sub_f32":
-            m.vwrite(args[0], m.vread(args[1]) - m.vread(args[2]))
-        elif op == "v_mul_f32":
-            with np.errstate(invalid="ignore"):
-                m.vwrite(args[0], m.vread(args[1]) * m.vread(args[2]))
-        elif op in ("v_max_f32", "v_max_f32_e64"):
-            m.vwrite(args[0], np.fmax(m.vread(args[1]), m.vread(args[2])))
-        elif op == "v_max3_f32":
-            m.vwrite(args[0], np.fmax(np.fmax(m.vread(args[1]), m.vread(args[2])),
-                                      m.vread(args[3])))
-        elif op == "v_mov_b32":
-            m.vwrite(args[0], m.vread_u(args[1]))
-        elif op == "v_dot2_f32_bf16":
-            x, y = m.vread_u(args[1]), m.vread_u(args[2])
-            prod = (bf16_to_f32(x & 0xFFFF).astype(np.float64) * bf16_to_f32(y & 0xFFFF)
-                    + bf16_to_f32(x >> 16).astype(np.float64) * bf16_to_f32(y >> 16))
-            m.vwrite(args[0], (prod + m.vread(args[3])).astype(np.float32))
-        elif op == "v_cvt_pk_bf16_f32":
-            lo_, hi_ = bf16_bits(m.vread(args[1])), bf16_bits(m.vread(args[2]))
-            m.vwrite(args[0], (lo_ | (hi_ << 16)).astype(np.uint32))
-        elif op == "v_cmp_lt_f32":
-            m.vcc = m.vread(args[1]) < m.vread(args[2])
-        elif op == "v_cmp_gt_i32_e64":
-            mask = np.int64(int(args[1])) > m.vread_u(args[2]).view(np.int32).astype(np.int64)
-            lo = int(REG.match(args[0]).group(3))
-            bits = int(sum(1 << l for l in range(64) if mask[l]))
-            m.s[lo], m.s[lo + 1] = bits & 0xFFFFFFFF, bits >> 32
-        elif op == "v_cndmask_b32_e64":
-            lo = int(REG.match(args[3]).group(3))
-            bits = m.s[lo] | (m.s[lo + 1] << 32)
-            mask = np.array([(bits >> l) & 1 for l in range(64)], bool)
-            m.vwrite(args[0], np.where(mask, m.vread_u(args[2]), m.vread_u(args[1])).astype(np.uint32))
-        elif op == "v_sub_u32_e64":
-            m.vwrite(args[0], (m.vread_u(args[1]) - np.uint32(int(args[2]))).astype(np.uint32))
-        elif op == "v_accvgpr_read_b32":
-            m.vwrite(args[0], m.vread_u(args[1]))
-        elif op == "v_accvgpr_write_b32":
-            _, _, lo, _ = m.rng(args[0])
-            m.a[lo] = m.vread_u(args[1])
-        else:
-            raise NotImplementedError(op)
-    return None
+PROGRAM = Program(LINES, ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"), "FA_SLOW")
 
 
 def emulate_workgroup(q, k, v, N, q0, causal, scale):
@@ -423,17 +120,11 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
         m.s[G.S_FM] = fm
         m.s[G.S_FAST] = max(0, min(fm - 1, (nt - 1 if tail else tend) - 2))
         m.s[G.S_J] = 0
-        waves.append([m, 0])
-    while True:
-        for w, wv in enumerate(waves):
-            wv[1] = run_wave(wv[0], lds, mem, wv[1], w)
-        done = [wv[1] is None for wv in waves]
-        assert all(done) or not any(done), "waves disagree on the barrier count"
-        if all(done):
-            break
+        waves.append(m)
+    PROGRAM.run_workgroup(waves, lds, mem)
     O = np.zeros((BR, D))
     L = np.full(BR, np.nan)
-    for w, (m, _) in enumerate(waves):
+    for w, m in enumerate(waves):
         lsum = m.v[G.LSUM:G.LSUM + 2].view(np.float32)
         mref = -m.v[G.MNEG:G.MNEG + 2].view(np.float32)
         for lane in range(64):
@@ -500,13 +191,13 @@ def test_generated_loop_matches_the_oracle(N, q0, causal, kscale):
         k[192:] *= kscale
         k = bf16_to_f32(bf16_bits(k))
     scale = D ** -0.5
-    SLOW_TAKEN[0] = 0
-    BODIES_RUN.clear()
+    PROGRAM.slow_taken = 0
+    PROGRAM.bodies_run.clear()
     O, L = emulate_workgroup(q, k, v, N, q0, causal, scale)
-    assert BODIES_RUN == expected_bodies(N, q0, causal), BODIES_RUN
+    assert [b[3:] for b in PROGRAM.bodies_run] == expected_bodies(N, q0, causal), PROGRAM.bodies_run
     # keys scaled by 3 from key 192 on lift those tiles' weights far past 2^8
     # above the reference set by tile 0: the exact slow path must run there
-    assert (SLOW_TAKEN[0] > 0) == (kscale != 1.0), SLOW_TAKEN[0]
+    assert (PROGRAM.slow_taken > 0) == (kscale != 1.0), PROGRAM.slow_taken
     rows = np.arange(q0, min(q0 + BR, N))
     ro, rl = oracle.forward(q[None], k[None], v[None], scale, causal)
     err = np.abs(O[rows - q0] - ro[0][rows])

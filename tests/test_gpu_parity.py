@@ -339,6 +339,40 @@ def test_backward_batched_d64(causal):
     backward_parity_all_heads(q, k, v, do, causal, chunk=32)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 129, 200, 333, 700])
+def test_backward_resident_dq_grid(N, causal):
+    """Enough heads (B2 H130: at least one 256-row query tile per CU) that the
+    dQ pass takes the resident hand-scheduled d = 128 kernel, at short and
+    ragged N: 1 to 11 key tiles per item, so its K/V stages start and end at
+    every tile index modulo 4, with masked, general and final steps."""
+    need_gpu()
+    log(f"backward bf16 B2 H130 N{N} d128 causal={causal} (resident dQ)")
+    q, k, v, do = inputs.qkv(2, 130, N, 128, torch.bfloat16, seed=3000 + N, with_dout=True)
+    backward_parity_all_heads(q, k, v, do, causal, chunk=65)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_resident_dq_grouped_heads(causal):
+    """Grouped K/V heads (130 query heads over 26) through the resident dQ
+    kernel: each query head reads its group's K and V."""
+    need_gpu()
+    log(f"gqa backward B2 H130 Hkv26 N333 d128 causal={causal} (resident dQ)")
+    gqa_parity(2, 130, 26, 333, 128, causal, seed=44)
+
+
+def test_backward_resident_dq_is_deterministic():
+    need_gpu()
+    q, k, v, do = (t.to(DEV) for t in inputs.qkv(2, 130, 333, 128, torch.bfloat16, seed=8,
+                                                 with_dout=True))
+    o, lse = _lib.forward(q, k, v, causal=True)
+    a = _lib.backward(q, k, v, o, do, lse, causal=True)
+    b = _lib.backward(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def test_backward_is_deterministic():
     need_gpu()
     q, k, v, do = (t.to(DEV) for t in inputs.qkv(2, 4, 1000, 128, torch.bfloat16, seed=9,
