@@ -942,7 +942,12 @@ hipError_t launch_mode(const BwdArgs& a, hipStream_t s) {
   const long long g2 = (long long)((a.N + DqTile<D>::BQ - 1) / DqTile<D>::BQ) * a.B * a.H;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (D == 128) {
-    hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, MODE>), dim3((unsigned)g1), dim3(512), 0, s, a);
+    if (!(MODE & kSparse) && dkdv128_applies(a)) {   // the resident kernel (fa_bwd_dkdv128.hip)
+      const hipError_t e = launch_dkdv128(a, s);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, MODE>), dim3((unsigned)g1), dim3(512), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves<D, MODE>, MODE>), dim3((unsigned)g1),
                        dim3(TK::THREADS), 0, s, a);

@@ -60,5 +60,7 @@ hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 bool dq128_applies(const BwdArgs& a);
 hipError_t launch_dq128(const BwdArgs& a, hipStream_t s);
+bool dkdv128_applies(const BwdArgs& a);
+hipError_t launch_dkdv128(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -1,6 +1,7 @@
 // fa_resident.hpp -- shared pieces of the d = 128 kernels whose workgroups
 // stay resident (one per CU) and run a generated, register-pinned key loop
-// between C++ set-up and epilogue: fa_fwd128.hip and fa_bwd_dq128.hip.
+// between C++ set-up and epilogue: fa_fwd128.hip, fa_bwd_dq128.hip and
+// fa_bwd_dkdv128.hip.
 //
 // The generated loop overwrites every vector register and most scalar ones,
 // so the C++ around it re-derives what it needs in each round of the
@@ -27,6 +28,19 @@ __device__ __forceinline__ void dma16_untracked(const void* gbase, uint32_t voff
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
   const uint32_t ms = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(ms), "v"(voff), "s"(gs)
+               : "memory", "m0");
+}
+
+// The same with 4 bytes per lane: lane l's 4 bytes at gbase + voff land at
+// LDS byte address m0 + 4 l.
+__device__ __forceinline__ void dma4_untracked(const void* gbase, uint32_t voff, uint32_t m0) {
+  const uint64_t g = reinterpret_cast<uint64_t>(gbase);
+  const uint64_t gs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
+  const uint32_t ms = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(ms), "v"(voff), "s"(gs)
                : "memory", "m0");
@@ -143,6 +157,14 @@ __device__ __forceinline__ void dma_rows128(const Shape& sh, const bf16* head, i
     const int col = 8 * ((lane & 15) ^ tile_swz<128>(row));
     dma16_untracked(head, (uint32_t)(min(r0 + row, sh.N - 1) * 128 + col) * 2u, lds + 1024u * i);
   }
+}
+
+// Direct loads of the 64 fp32 values of tile t of a per-row vector (one
+// head's LSE or D) into 256 bytes of LDS at byte `lds` (rows past the
+// sequence repeat its last row).
+__device__ __forceinline__ void dma_vec64(const Shape& sh, const float* src, int t, uint32_t lds) {
+  const int lane = fresh_lane();
+  dma4_untracked(src + (size_t)t * 64, (uint32_t)(min(lane, sh.N - 1 - t * 64) * 4), lds);
 }
 
 // Resident workgroups: one per CU (each takes a whole CU's registers).

@@ -1,5 +1,6 @@
 """Instruction-level CPU emulation of the generated inline-assembly loops
-(fa_fwd128_loop.inc, fa_bwd_dq128_loop.inc), shared by their tests.
+(fa_fwd128_loop.inc, fa_bwd_dq128_loop.inc, fa_bwd_dkdv128_loop.inc),
+shared by their tests.
 
 The instruction text is executed for the four waves of one workgroup on a
 model of their registers, the workgroup's LDS and global buffers:
@@ -8,8 +9,8 @@ model of their registers, the workgroup's LDS and global buffers:
   * v_mfma_f32_32x32x16_bf16 with the operand and accumulator layouts
     measured on the device (fa_common.hpp);
   * ds_read_b128 / ds_read_b64_tr_b16 / ds_bpermute_b32 and the direct
-    HBM -> LDS loads (global_load_lds_dwordx4 with M0 and an instruction
-    offset that applies to both addresses);
+    HBM -> LDS loads (global_load_lds_dwordx4 / _dword with M0 and an
+    instruction offset that applies to both addresses);
   * s_barrier: every wave runs up to its next barrier before any goes on.
 Every global load is checked to lie inside a registered buffer and every LDS
 access inside LDS.  Hazards and timing are not modelled.
@@ -116,11 +117,14 @@ class Memory:
     def __init__(self, bufs):
         self.bufs = bufs   # list of (base address, uint8 array)
 
-    def read16(self, addr):
+    def read(self, addr, n):
         for base, arr in self.bufs:
-            if base <= addr and addr + 16 <= base + arr.size:
-                return arr[addr - base: addr - base + 16]
-        raise AssertionError(f"global load outside the K/V buffers at {addr:#x}")
+            if base <= addr and addr + n <= base + arr.size:
+                return arr[addr - base: addr - base + n]
+        raise AssertionError(f"global load outside the buffers at {addr:#x}")
+
+    def read16(self, addr):
+        return self.read(addr, 16)
 
 
 def parse(lines):
@@ -244,6 +248,21 @@ class Program:
                     dst = m.m0 + off + 16 * l
                     assert 0 <= dst and dst + 16 <= lds.size, "LDS write out of range"
                     lds[dst:dst + 16] = data
+            elif op == "global_load_lds_dword":
+                lo = int(REG.match(args[1]).group(3))
+                base = m.s[lo] | (m.s[lo + 1] << 32)
+                voff = m.vread_u(args[0])
+                for l in range(64):
+                    data = mem.read(base + int(voff[l]) + off, 4)
+                    dst = m.m0 + off + 4 * l
+                    assert 0 <= dst and dst + 4 <= lds.size, "LDS write out of range"
+                    lds[dst:dst + 4] = data
+            elif op == "s_mov_b32":
+                m.swrite(args[0], m.sval(args[1]))
+            elif op == "s_lshl_b32":
+                t = m.sval(args[1]) << m.sval(args[2])
+                m.scc = int((t & 0xFFFFFFFF) != 0)
+                m.swrite(args[0], t)
             elif op == "ds_read_b128":
                 arr, lo, _ = m.block(args[0])
                 addr = m.vread_u(args[1]) + off
@@ -308,6 +327,15 @@ class Program:
                 bits = m.s[lo] | (m.s[lo + 1] << 32)
                 mask = np.array([(bits >> l) & 1 for l in range(64)], bool)
                 m.vwrite(args[0], np.where(mask, m.vread_u(args[2]), m.vread_u(args[1])).astype(np.uint32))
+            elif op == "v_cmp_ge_u32_e64":
+                mask = m.vread_u(args[1]) >= m.vread_u(args[2])
+                lo = int(REG.match(args[0]).group(3))
+                bits = int(sum(1 << l for l in range(64) if mask[l]))
+                m.s[lo], m.s[lo + 1] = bits & 0xFFFFFFFF, bits >> 32
+            elif op == "v_sub_u32":
+                m.vwrite(args[0], (m.vread_u(args[1]) - m.vread_u(args[2])).astype(np.uint32))
+            elif op == "v_subrev_u32":
+                m.vwrite(args[0], (m.vread_u(args[2]) - m.vread_u(args[1])).astype(np.uint32))
             elif op == "v_sub_u32_e64":
                 m.vwrite(args[0], (m.vread_u(args[1]) - np.uint32(int(args[2]))).astype(np.uint32))
             elif op == "v_accvgpr_read_b32":

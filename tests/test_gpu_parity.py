@@ -341,13 +341,14 @@ def test_backward_batched_d64(causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 65, 129, 200, 333, 700])
-def test_backward_resident_dq_grid(N, causal):
-    """Enough heads (B2 H130: at least one 256-row query tile per CU) that the
-    dQ pass takes the resident hand-scheduled d = 128 kernel, at short and
-    ragged N: 1 to 11 key tiles per item, so its K/V stages start and end at
-    every tile index modulo 4, with masked, general and final steps."""
+def test_backward_resident_grid(N, causal):
+    """Enough heads (B2 H130: at least one 256-row query tile and one 128-key
+    block per CU) that the dQ and dK/dV passes take the resident
+    hand-scheduled d = 128 kernels, at short and ragged N: 1 to 11 tiles per
+    item, so their stages start and end at every tile index modulo 4, with
+    masked, general and final steps, and partial key blocks."""
     need_gpu()
-    log(f"backward bf16 B2 H130 N{N} d128 causal={causal} (resident dQ)")
+    log(f"backward bf16 B2 H130 N{N} d128 causal={causal} (resident dQ, dK/dV)")
     q, k, v, do = inputs.qkv(2, 130, N, 128, torch.bfloat16, seed=3000 + N, with_dout=True)
     backward_parity_all_heads(q, k, v, do, causal, chunk=65)
 
@@ -361,7 +362,18 @@ def test_backward_resident_dq_grouped_heads(causal):
     gqa_parity(2, 130, 26, 333, 128, causal, seed=44)
 
 
-def test_backward_resident_dq_is_deterministic():
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_resident_long(causal):
+    """The resident d = 128 backward kernels over long sequences (B2 H16
+    N2048: 32 query tiles per dK/dV item, 32 key tiles per dQ item), every
+    head."""
+    need_gpu()
+    log(f"backward bf16 B2 H16 N2048 d128 causal={causal} (resident), all heads")
+    q, k, v, do = inputs.qkv(2, 16, 2048, 128, torch.bfloat16, seed=77, with_dout=True)
+    backward_parity_all_heads(q, k, v, do, causal, chunk=8)
+
+
+def test_backward_resident_is_deterministic():
     need_gpu()
     q, k, v, do = (t.to(DEV) for t in inputs.qkv(2, 130, 333, 128, torch.bfloat16, seed=8,
                                                  with_dout=True))
