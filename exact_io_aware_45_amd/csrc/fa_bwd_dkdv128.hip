@@ -16,10 +16,10 @@
 //     mask the first key blocks, which see the most queries, go first); each
 //     wave owns 32 keys: their K and V rows and their dK^T, dV^T
 //     accumulators sit in the accumulation registers;
-//   * Q and dO tiles (64 queries) load two tiles ahead, HBM -> LDS by direct
-//     loads, into four stages each (a tile is read as rows for the scores and,
-//     half a tile later, transposed for the gradients), and each wave's copy
-//     of the tile's L and D values beside them;
+//   * Q and dO tiles (64 queries) load three tiles ahead, HBM -> LDS by
+//     direct loads, into four stages each (a tile is read as rows for the
+//     scores and, half a tile later, transposed for the gradients), and each
+//     wave's copy of the tile's L and D values beside them;
 //   * the query loop is one generated statement (fa_bwd_dkdv128_loop.inc,
 //     from gen_bwd_dkdv128.py).  The C++ below loads the item's K and V rows,
 //     sets up addresses and loop bounds, and stores dK and dV.
@@ -50,35 +50,34 @@ void bwd_dkdv128_kernel(BwdArgs a) {
   // LDS, bytes: [0, 64K) Q stages 0-3, [64K, 128K) dO stages 0-3, [128K,
   // 136K) L/D stages 0-3 of 2 KiB (wave w's 64 L values at 512 w, its D
   // values 256 bytes further).  The generated loop addresses these directly.
+  // After the loop, [32K w, 32K (w + 1)) stages wave w's dK and dV rows.
   __shared__ __attribute__((aligned(1024))) bf16 smem[8 * TILE + 4096];
   constexpr uint32_t OST0 = 4 * TILE_BYTES, LST0 = 8 * TILE_BYTES;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto lds_base = [&]() {
     return fresh(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem)));
   };
-
-  for (int r = 0;; ++r) {
-    const Shape sh = fresh_shape<BK, BQ>(a.N, a.B, a.H, a.Hkv);
-    Item cur;
-    if (!resident_item<CAUSAL, BK>(sh, r, cur)) break;
-    const int N = sh.N, nt = sh.nt;
+  auto shape = [&]() { return fresh_shape<BK, BQ>(a.N, a.B, a.H, a.Hkv); };
+  // Key block of an item: with a causal mask, item rank 0 (handed out first)
+  // is key block 0, which sees every query.
+  auto key0_of = [&](const Shape& sh, const Item& it) {
+    return CAUSAL ? (sh.nq - 1) * BK - it.q0 : it.q0;
+  };
+  // The item's query tiles ts .. ts + 2 into stages 0 .. 2, and this wave's
+  // copy of their L and D values (the LDS they fill is free: the previous
+  // item's loop and epilogue ended with a barrier after their last read).
+  auto dma_first_tiles = [&](const Shape& sh, const Item& it) {
     const int wave = fresh(wave0);
     const uint32_t lds0 = lds_base();
-    // Key block of the item: with a causal mask, item rank 0 (handed out
-    // first) is key block 0, which sees every query.
-    const int k0 = CAUSAL ? (sh.nq - 1) * BK - cur.q0 : cur.q0;
-    const int ts = CAUSAL ? k0 / BQ : 0;   // first query tile that sees a key of the block
-    const int cnt = nt - ts;               // query tiles of the item
-    const size_t head = (size_t)cur.bh * (size_t)N * D;
-    const bf16* __restrict__ Q = fresh(reinterpret_cast<const bf16*>(a.q)) + head;
-    const bf16* __restrict__ dO = fresh(reinterpret_cast<const bf16*>(a.dout)) + head;
-    const float* lse2 = fresh(a.lse2) + (size_t)cur.bh * N;
-    const float* del = fresh(a.delta) + (size_t)cur.bh * N;
-
-    // Query tiles ts and ts + 1 into stages 0 and 1 (the previous item's loop
-    // ended with a barrier after its last LDS read).
+    const int ts = CAUSAL ? key0_of(sh, it) / BQ : 0;
+    const int cnt = sh.nt - ts;
+    const size_t head = (size_t)it.bh * (size_t)sh.N * D;
+    const bf16* Q = fresh(reinterpret_cast<const bf16*>(a.q)) + head;
+    const bf16* dO = fresh(reinterpret_cast<const bf16*>(a.dout)) + head;
+    const float* lse2 = fresh(a.lse2) + (size_t)it.bh * sh.N;
+    const float* del = fresh(a.delta) + (size_t)it.bh * sh.N;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 3; ++s) {
       if (s < cnt) {
         dma_tile128(sh, wave, Q, ts + s, lds0 + s * TILE_BYTES);
         dma_tile128(sh, wave, dO, ts + s, lds0 + OST0 + s * TILE_BYTES);
@@ -86,6 +85,30 @@ void bwd_dkdv128_kernel(BwdArgs a) {
         dma_vec64(sh, del, ts + s, lds0 + LST0 + 2048u * s + 512u * wave + 256u);
       }
     }
+  };
+
+  Item cur;
+  {
+    const Shape sh = shape();
+    if (!resident_item<CAUSAL, BK>(sh, 0, cur)) return;
+    dma_first_tiles(sh, cur);
+  }
+
+  for (int r = 0;; ++r) {
+    const Shape sh = shape();
+    Item nxt;
+    const bool more = resident_item<CAUSAL, BK>(sh, r + 1, nxt);
+    const int N = sh.N, nt = sh.nt;
+    const int wave = fresh(wave0);
+    const uint32_t lds0 = lds_base();
+    const int k0 = key0_of(sh, cur);
+    const int ts = CAUSAL ? k0 / BQ : 0;   // first query tile that sees a key of the block
+    const int cnt = nt - ts;               // query tiles of the item
+    const size_t head = (size_t)cur.bh * (size_t)N * D;
+    const bf16* __restrict__ Q = fresh(reinterpret_cast<const bf16*>(a.q)) + head;
+    const bf16* __restrict__ dO = fresh(reinterpret_cast<const bf16*>(a.dout)) + head;
+    const float* lse2 = fresh(a.lse2) + (size_t)cur.bh * N;
+    const float* del = fresh(a.delta) + (size_t)cur.bh * N;
 
     // This wave's K and V rows: lane (l32, h) holds key k0 + 32 wave + l32,
     // d = 16 c + 8 h .. +7 (keys past the sequence repeat its last one; their
@@ -158,15 +181,14 @@ void bwd_dkdv128_kernel(BwdArgs a) {
     const uint32_t m0q = uni(lds0 + wave * 4096);
     const uint32_t m0o = uni(lds0 + OST0 + wave * 4096);
     const uint32_t m0l = uni(lds0 + LST0 + wave * 512);
-    uint32_t cbits;   // scale * log2(e), computed on the vector unit, read back explicitly
-    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(cbits) : "v"(fresh(a.scale) * kLog2e));
-    uint64_t qptr = uni64(reinterpret_cast<uint64_t>(Q + (size_t)(ts + 2) * TILE));
-    uint64_t optr = uni64(reinterpret_cast<uint64_t>(dO + (size_t)(ts + 2) * TILE));
-    uint64_t lptr = uni64(reinterpret_cast<uint64_t>(lse2 + (size_t)(ts + 2) * BQ));
+    const uint32_t cbits = uniform_bits(fresh(a.scale) * kLog2e);   // scale * log2(e)
+    uint64_t qptr = uni64(reinterpret_cast<uint64_t>(Q + (size_t)(ts + 3) * TILE));
+    uint64_t optr = uni64(reinterpret_cast<uint64_t>(dO + (size_t)(ts + 3) * TILE));
+    uint64_t lptr = uni64(reinterpret_cast<uint64_t>(lse2 + (size_t)(ts + 3) * BQ));
     // The D load carries instruction offset 256 (its LDS area follows L's).
-    uint64_t dptr = uni64(reinterpret_cast<uint64_t>(del + (size_t)(ts + 2) * BQ) - 256u);
+    uint64_t dptr = uni64(reinterpret_cast<uint64_t>(del + (size_t)(ts + 3) * BQ) - 256u);
     // Loop control, in tiles relative to ts: step j processes tile j and
-    // loads tile j + 2; the partial last tile (loaded by step cnt - 3) goes
+    // loads tile j + 3; the partial last tile (loaded by step cnt - 4) goes
     // through the clamped offsets; tiles below `mlo` (the causal diagonal) and
     // from `mhi` on (the partial last tile) need a mask; steps mlo <= j <
     // sfast need none and load whole tiles.
@@ -174,15 +196,15 @@ void bwd_dkdv128_kernel(BwdArgs a) {
     const int mhi = sh.ragged ? cnt - 1 : cnt;
     uint32_t jt = 0;
     const uint32_t slast = uni((uint32_t)(cnt - 1));
-    const uint32_t skend = uni((uint32_t)max(0, cnt - 2));
-    const uint32_t stailj = uni(sh.ragged && cnt >= 3 ? (uint32_t)(cnt - 3) : ~0u);
+    const uint32_t skend = uni((uint32_t)max(0, cnt - 3));
+    const uint32_t stailj = uni(sh.ragged && cnt >= 4 ? (uint32_t)(cnt - 4) : ~0u);
     const uint32_t smlo = uni((uint32_t)mlo);
     const uint32_t smhi = uni((uint32_t)mhi);
-    const uint32_t sfast = uni((uint32_t)max(0, mhi - 2));
+    const uint32_t sfast = uni((uint32_t)max(0, mhi - 3));
     const uint32_t smask0 = uni((mlo > 0 || mhi == 0) ? 1u : 0u);
     const float ninf = -INFINITY;
     wait_vmem();
-    __syncthreads();   // tiles 0 and 1 are in LDS for every wave
+    __syncthreads();   // tiles 0 .. 2 are in LDS for every wave
 
     f32x16 dk[4], dv[4];
     asm volatile(FA_BWD_DKDV128_LOOP_ASM
@@ -206,35 +228,61 @@ void bwd_dkdv128_kernel(BwdArgs a) {
                    "{s89}"(smask0)
                  : FA_BWD_DKDV128_LOOP_CLOBBERS);
 
-    // dK = scale * acc, dV = acc, fp32: lane (l32, h) of block db holds
-    // d = 32 db + 8 g + 4 h .. +3 in registers 4g .. 4g + 3.
-    const Shape sh2 = fresh_shape<BK, BQ>(a.N, a.B, a.H, a.Hkv);
+    // Epilogue: dK = scale * acc, dV = acc, fp32.  Lane (l32, h) of block db
+    // holds key l32, d = 32 db + 8 g + 4 h .. +3 in registers 4g .. 4g + 3:
+    // stored as it is, every instruction would write 32 B pieces of 32 rows.
+    // Each wave passes its 32 rows of dK and of dV through its own 32 KiB of
+    // LDS instead (16-byte chunk q of row k at slot q ^ k, so that the writes
+    // of 32 rows and the reads of 2 whole rows both spread over the banks)
+    // and stores 1 KiB of two consecutive rows per instruction.
+    const Shape sh2 = shape();
+    const int wave2 = fresh(wave0);
     const int el = fresh_lane(), eh = el >> 5, e32 = el & 31;
-    const int key2 = (CAUSAL ? (sh2.nq - 1) * BK - cur.q0 : cur.q0) + 32 * fresh(wave0) + e32;
     const float sc = fresh(a.scale);
     // dV passes through a multiply by an opaque 1 too: a plain copy out of the
     // accumulation registers is not lowered correctly (it becomes a vector
     // move with a 16-register source).
     const float one = fresh(1.0f);
-    typedef __attribute__((address_space(1))) f32x4 gf32x4;
-    if (key2 < sh2.N) {
-      const size_t row = ((size_t)cur.bh * sh2.N + key2) * D + 4 * eh;
-      gf32x4* dkp = (gf32x4*)(fresh(a.dk) + row);
-      gf32x4* dvp = (gf32x4*)(fresh(a.dv) + row);
+    FA_LDS char* stg = (FA_LDS char*)smem + 32768 * wave2;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 x, y;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x, y;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = dk[db][4 * g + e] * sc;
-            y[e] = dv[db][4 * g + e] * one;
-          }
-          dkp[(32 * db + 8 * g) / 4] = x;
-          dvp[(32 * db + 8 * g) / 4] = y;
+        for (int e = 0; e < 4; ++e) {
+          x[e] = dk[db][4 * g + e] * sc;
+          y[e] = dv[db][4 * g + e] * one;
         }
+        const int slot = 16 * ((8 * db + 2 * g + eh) ^ e32);
+        *reinterpret_cast<FA_LDS f32x4*>(stg + 512 * e32 + slot) = x;
+        *reinterpret_cast<FA_LDS f32x4*>(stg + 16384 + 512 * e32 + slot) = y;
+      }
+    f32x4 rk[16], rv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + eh;
+      const int slot = 16 * (e32 ^ row);
+      rk[i] = *reinterpret_cast<const FA_LDS f32x4*>(stg + 512 * row + slot);
+      rv[i] = *reinterpret_cast<const FA_LDS f32x4*>(stg + 16384 + 512 * row + slot);
     }
+    __syncthreads();   // every wave has its rows: the LDS takes the next item's tiles
+    if (more) dma_first_tiles(sh2, nxt);
+    const int kw = key0_of(sh2, cur) + 32 * wave2;
+    typedef __attribute__((address_space(1))) f32x4 gf32x4;
+    const size_t row0 = ((size_t)cur.bh * sh2.N + kw + eh) * D + 4 * e32;
+    gf32x4* dkp = (gf32x4*)(fresh(a.dk) + row0);
+    gf32x4* dvp = (gf32x4*)(fresh(a.dv) + row0);
+    const int rows = sh2.N - kw;   // rows of this wave inside the sequence
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (2 * i + eh < rows) {
+        dkp[i * (2 * D / 4)] = rk[i];
+        dvp[i * (2 * D / 4)] = rv[i];
+      }
+    }
+    if (!more) break;
+    cur = nxt;
   }
 }
 

@@ -168,8 +168,7 @@ void bwd_dq128_kernel(BwdArgs a) {
     };
     const uint32_t m0k = uni(lds0 + wave * 4096);
     const uint32_t m0v = uni(lds0 + VST0 + wave * 4096);
-    uint32_t cbits;   // scale * log2(e), computed on the vector unit, read back explicitly
-    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(cbits) : "v"(fresh(a.scale) * kLog2e));
+    const uint32_t cbits = uniform_bits(fresh(a.scale) * kLog2e);   // scale * log2(e)
     uint64_t kptr = uni64(reinterpret_cast<uint64_t>(K + 2 * (size_t)TILE));
     uint64_t vptr = uni64(reinterpret_cast<uint64_t>(V + 2 * (size_t)TILE));
     // Loop control: step j processes tile j and loads tile j + 2 (K and V);

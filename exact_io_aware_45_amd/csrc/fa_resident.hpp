@@ -21,13 +21,15 @@ namespace fa {
 // One direct HBM -> LDS load of 16 bytes per lane: lane l's bytes at
 // gbase + voff land at LDS byte address m0 + 16 l.  The caller waits
 // (s_waitcnt vmcnt) and synchronises before any wave reads them, and issues
-// it only once every read of that LDS has returned.
+// it only once every read of that LDS has returned.  The wait states before
+// the load cover M0 and a base the vector unit may have just written to a
+// scalar register (readfirstlane): the compiler adds none for the statement.
 __device__ __forceinline__ void dma16_untracked(const void* gbase, uint32_t voff, uint32_t m0) {
   const uint64_t g = reinterpret_cast<uint64_t>(gbase);
   const uint64_t gs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
   const uint32_t ms = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(ms), "v"(voff), "s"(gs)
                : "memory", "m0");
@@ -40,10 +42,20 @@ __device__ __forceinline__ void dma4_untracked(const void* gbase, uint32_t voff,
   const uint64_t gs = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(g >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
   const uint32_t ms = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(ms), "v"(voff), "s"(gs)
                : "memory", "m0");
+}
+
+// A vector value that is the same in every lane, as scalar bits (read from
+// the first lane).  The wait states in front cover the hazard of reading a
+// register the vector unit has just written: the compiler does not look
+// inside the statement, so it inserts none of its own.
+__device__ __forceinline__ uint32_t uniform_bits(float x) {
+  uint32_t s;
+  asm volatile("s_nop 4\n\tv_readfirstlane_b32 %0, %1" : "=s"(s) : "v"(x));
+  return s;
 }
 
 // The lane index, recomputed where it is called (the statement is opaque).

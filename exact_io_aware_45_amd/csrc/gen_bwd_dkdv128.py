@@ -25,10 +25,11 @@ gen_fwd128.py, and the half-tile pipeline the dQ loop's, gen_bwd_dq128.py):
 Step 1 of query tile j: the exponentials and dS of (j, second half) beside
 the products dV/dK of (j, first half) and S/dP of (j + 1, first half); step 2:
 the vector work of (j + 1, first half) beside dV/dK of (j, second half) and
-S/dP of (j + 1, second half).  One barrier per tile.  Q, dO and the L, D rows
-of tile j + 2 load while tiles j and j + 1 are in use (four stages; the body
-is generated for each tile index modulo 4, counted from the item's first
-query tile).  Scores whose key follows the query (causal) or whose query
+S/dP of (j + 1, second half).  One barrier per tile.  Tile step j reads
+tiles j and j + 1 only, so with four LDS stages Q, dO and the L, D rows of
+tile j + 3 load during step j and have until the end of step j + 1 to land
+(the body is generated for each tile index modulo 4, counted from the
+item's first query tile).  Scores whose key follows the query (causal) or whose query
 lies past the sequence become -inf before the exponential, in the first two
 tiles of a causal item and in a partial last tile.
 """
@@ -73,7 +74,7 @@ NINF = 208        # v208: -inf
 TMP = 209         # v[209:216] temporaries of the mask test
 
 RING = 4          # slots per operand ring
-LEAD = 6          # products between an operand's read and its product
+LEAD = 5          # products between an operand's read and its product
 
 S_QPTR = 60       # s[60:61] global address of the next Q tile to load
 S_OPTR = 62       # s[62:63] the same for dO
@@ -81,7 +82,7 @@ S_M0Q = 64        # LDS byte address of this wave's slice of Q stage 0
 S_M0O = 65        # ... of dO stage 0
 S_C = 66          # scale * log2(e) (fp32 bits)
 S_LAST = 67       # relative index of the last query tile
-S_KEND = 68       # steps j >= this load no tile
+S_KEND = 68       # steps j >= this load no tile (tile j + 3 does not exist)
 S_TAILJ = 69      # step whose loads are the partial last tile (~0 when none)
 S_MLO = 70        # tiles before this need a mask (causal diagonal)
 S_J = 71          # relative index of the current query tile
@@ -89,6 +90,7 @@ S_MHI = 72        # tiles from this on need a mask (partial last tile)
 S_T = 73          # scratch
 S_MASK = (74, 76, 78, 80)
 S_FAST = 82       # straight steps: S_MLO <= j < S_FAST
+NLOAD = 10        # direct loads of one tile step (Q 4, dO 4, L 1, D 1)
 S_LPTR = 84       # s[84:85] global address of the next L row
 S_DPTR = 86       # s[86:87] ... of the next D row
 S_M0L = 88        # LDS byte address of this wave's L/D area of stage 0
@@ -244,44 +246,150 @@ def elem_half(x):
 
 
 # ------------------------------------------------------------------ steps
-def products(st, lds, sdp, grad, lv, valu, raw_sched=None):
-    """One step: the S/dP products of sdp = (stage, half, dst slot) (16,
-    reading Q and dO rows) and the dV/dK products of grad = (stage, half,
-    P/dS slot) (16, reading dO^T and Q^T), interleaved as S, dV, dP, dK per d
-    chunk: the two sets touch disjoint registers, and interleaving spreads
-    the row and transpose reads evenly.  Each product's operand reads go out
-    LEAD products ahead of it; the L/D reads lv = (stage, half, slot) for
-    the next step's vector work one every other product; `valu` fills the
-    issue slots beside them.  Ends with every LDS read landed."""
-    units = []
+def units_of(sdp, grad):
+    """The products of one step with their operand reads: the S/dP products
+    of sdp = (stage, half, dst slot) (16, reading Q and dO rows) and the
+    dV/dK products of grad = (stage, half, P/dS slot) (16, reading dO^T and
+    Q^T).  The two sets touch disjoint registers; pairs of them alternate
+    (spreading the row and transpose reads evenly), the gradient pairs one
+    pair ahead: their operands are in LDS before the barrier that publishes
+    the next tile, so the first products of a tile step need no read issued
+    after it."""
+    g, sd = [], []
+    if grad:
+        g_stg, g_half, src = grad
+        for i in range(8):
+            g.append([(grad_mfma("O", i, src),
+                       [(("TO", i, hi), r) for hi, r in enumerate(tr_reads("O", i, g_stg, g_half))]),
+                      (grad_mfma("Q", i, src),
+                       [(("TQ", i, hi), r) for hi, r in enumerate(tr_reads("Q", i, g_stg, g_half))])])
+    if sdp:
+        s_stg, s_half, dst = sdp
+        for i in range(8):
+            sd.append([(sdp_mfma("Q", i, dst), [(("Q", i), row_read("Q", i, s_stg, s_half))]),
+                       (sdp_mfma("O", i, dst), [(("O", i), row_read("O", i, s_stg, s_half))])])
+    if not g or not sd:
+        return [u for pair in g + sd for u in pair]
+    order = g[:1]
     for i in range(8):
-        if sdp:
-            s_stg, s_half, dst = sdp
-            units.append((sdp_mfma("Q", i, dst), [(("Q", i), row_read("Q", i, s_stg, s_half))]))
-        if grad:
-            g_stg, g_half, src = grad
-            units.append((grad_mfma("O", i, src),
-                          [(("TO", i, hi), r) for hi, r in enumerate(tr_reads("O", i, g_stg, g_half))]))
-        if sdp:
-            units.append((sdp_mfma("O", i, dst), [(("O", i), row_read("O", i, s_stg, s_half))]))
-        if grad:
-            units.append((grad_mfma("Q", i, src),
-                          [(("TQ", i, hi), r) for hi, r in enumerate(tr_reads("Q", i, g_stg, g_half))]))
+        order += g[i + 1:i + 2] + sd[i:i + 1]
+    return [u for pair in order for u in pair]
+
+
+PRE = 4   # leading gradient products of a tile step whose reads the previous step issues
+
+
+def pre_rids():
+    """Ids of the reads a tile step finds in flight when it starts (issued
+    at the end of the step before it, in this order)."""
+    return [rid for _, reads in units_of(None, (0, 0, 0))[:PRE] for rid, _ in reads]
+
+
+def products(st, lds, units, lv, valu, raw_sched=None, pre=0, nxt=None):
+    """Issue `units` (a list from units_of) with `valu` in the issue slots
+    beside them.  Each product's operand reads go out LEAD products ahead of
+    it: the reads of the first `pre` units were issued before this call, and
+    the reads of the first nxt[0] units of the list nxt[1] (the next call's)
+    go out in this call's last products.  The L/D reads lv = (stage, half,
+    slot) for the next step's vector work go out one every other product."""
     mf = [m for m, _ in units]
     need = {p: {rid for rid, _ in reads} for p, (_, reads) in enumerate(units)}
     before, sched = [], {}
     for p, (_, reads) in enumerate(units):
+        if p < pre:
+            continue
         if p < LEAD:
             before += reads
         else:
             sched.setdefault(p - LEAD, []).extend(reads)
+    if nxt:
+        n, later = nxt
+        for p in range(n):
+            sched.setdefault(len(mf) - LEAD + p, []).extend(later[p][1])
     if lv:
         stg, half, x = lv
         for i, rd in enumerate(lv_reads(stg, half, x)):
-            sched.setdefault(min(2 * i + 1, len(mf) - 1), []).append(rd)
-    F.interleave(st, mf, before, valu, lds, sched, need, raw_sched=raw_sched)
-    st.raw("s_waitcnt lgkmcnt(0)")
-    lds.pending.clear()
+            sched.setdefault(min(2 * i + 1, len(mf) - LEAD - 1), []).append(rd)
+    interleave_even(st, mf, before, valu, lds, sched, need, raw_sched=raw_sched)
+
+
+GAP = 28.0        # most issue cycles of other work between two products
+INIT = 0.0        # vector work before the first product of a call
+
+
+def interleave_even(st, mfmas, reads_before, valu, lds, read_sched, operand_reads,
+                    raw_sched=None):
+    """Emit the products in order; after product i the LDS reads scheduled
+    for it, the scalar/load lines raw_sched[i], then vector work.  Unlike
+    the forward's filler, which packs each product's shadow full, the
+    vector work is spread evenly: after product i it takes the remaining
+    work's share of the remaining products (at most GAP cycles with the
+    reads and scalar lines), so the matrix pipe never waits on a burst and
+    no work is left for the end.  A product waits (s_waitcnt) until its
+    operand reads have landed."""
+    raw_sched = raw_sched or {}
+    valu = list(valu)
+
+    def ready(i):
+        ins = valu[i]
+        if st.need(ins) > 0:
+            return False
+        for prev in valu[:i]:
+            if (ins.uses | ins.srcc) & prev.defs or ins.defs & (prev.uses | prev.srcc | prev.defs):
+                return False
+        return True
+
+    def fill(budget):
+        used = 0.0
+        while valu:
+            pick = next((i for i in range(min(F.LOOKAHEAD, len(valu))) if ready(i)), None)
+            if pick is None or used + valu[pick].cost > budget + 1e-9:
+                break
+            ins = valu.pop(pick)
+            st.emit(ins)
+            used += ins.cost
+
+    for rid, ins in reads_before:
+        st.emit(ins)
+        lds.issue(rid)
+    if mfmas and INIT:
+        fill(INIT)
+    n = len(mfmas)
+    for i, mf in enumerate(mfmas):
+        k = lds.wait_for(operand_reads[i])
+        if k is not None:
+            st.raw(f"s_waitcnt lgkmcnt({min(k, 15)})")
+        st.emit(mf)
+        spent = 0.0
+        for rid, ins in read_sched.get(i, []):
+            st.emit(ins)
+            lds.issue(rid)
+            spent += ins.cost
+        for line in raw_sched.get(i, []):
+            st.raw(line)
+            spent += F.COST["vmem"] if line.startswith("global_") else F.COST["salu"]
+        left = sum(x.cost for x in valu)
+        share = left / max(1, n - i)
+        fill(min(GAP - spent, share + 4.5))
+    for ins in valu:
+        st.emit(ins)
+
+
+def end_step(st, lds, last):
+    """Wait for every LDS read but the next step's first operands (none
+    after the last step), which must be the last reads in flight."""
+    keep = [] if last else pre_rids()
+    assert lds.pending[len(lds.pending) - len(keep):] == keep, lds.pending
+    st.raw(f"s_waitcnt lgkmcnt({len(keep)})")
+    lds.pending = list(keep)
+
+
+def wait_lv(st, lds, lv):
+    """Wait until the L/D reads lv = (stage, half, slot) have landed."""
+    stg, half, x = lv
+    k = lds.wait_for({rid for rid, _ in lv_reads(stg, half, x)})
+    if k is not None:
+        st.raw(f"s_waitcnt lgkmcnt({min(k, 15)})")
 
 
 def full_loads(stage):
@@ -316,6 +424,8 @@ def tail_loads(stage):
 
 
 def load_block(st, stage, uid):
+    """Loads of tile j + 3 in a body other than the straight one: none past
+    the end, the clamped ones for the partial last tile, else whole."""
     skip, tail, done = f"FK_SKIP{uid}_%=", f"FK_TAIL{uid}_%=", f"FK_LDONE{uid}_%="
     st.raw(f"s_cmp_ge_u32 s{S_J}, s{S_KEND}")
     st.raw(f"s_cbranch_scc1 {skip}")
@@ -344,7 +454,8 @@ def iteration(out, p, kind, name):
     """Query tile step j (j % 4 = p): kind "fast", "gen", "masked" or "final"."""
     st = Stream(out)
     lds = LdsCounter()
-    sj, sn, sl = p % 4, (p + 1) % 4, (p + 2) % 4
+    lds.pending = pre_rids()
+    sj, sn, sl = p % 4, (p + 1) % 4, (p + 3) % 4
     final = kind == "final"
     masked = kind in ("masked", "final")
     raw = None
@@ -357,19 +468,39 @@ def iteration(out, p, kind, name):
         load_block(st, sl, name)
     # step 1: vector work of (j, second half); dV/dK of (j, first half);
     # S/dP of (j + 1, first half); L/D of (j + 1, first half)
+    u1 = units_of(None if final else (sn, 0, 0), (sj, 0, 0))
+    u2 = units_of(None if final else (sn, 1, 1), (sj, 1, 1))
+    lv1 = None if final else (sn, 0, 0)
     if masked:
         mask_setup(st, 32)
     valu = (mask_ops(1, 1) if masked else []) + elem_half(1)
-    products(st, lds, None if final else (sn, 0, 0), (sj, 0, 0),
-             None if final else (sn, 0, 0), valu, raw)
+    products(st, lds, u1, lv1, valu, raw, pre=PRE, nxt=(LEAD, u2))
     # step 2: vector work of (j + 1, first half); dV/dK of (j, second half);
-    # S/dP of (j + 1, second half); L/D of (j + 1, second half)
+    # S/dP of (j + 1, second half); L/D of (j + 1, second half); the reads
+    # of the next step's first gradient products
+    if not final:
+        wait_lv(st, lds, lv1)
     if masked and not final:
         mask_setup(st, 64)
     valu = [] if final else ((mask_ops(0, 0) if masked else []) + elem_half(0))
-    products(st, lds, None if final else (sn, 1, 1), (sj, 1, 1),
-             None if final else (sn, 1, 1), valu)
-    st.raw("s_waitcnt vmcnt(0)")
+    nxt = None if final else (PRE, units_of(None, (sn, 0, 0)))
+    products(st, lds, u2, None if final else (sn, 1, 1), valu, pre=LEAD, nxt=nxt)
+    end_step(st, lds, final)
+    # tile j + 2 (loaded by the step before) must have landed before the
+    # barrier publishes it; this step's loads (tile j + 3) may stay in flight
+    if kind == "fast":
+        st.raw(f"s_waitcnt vmcnt({NLOAD})")
+    elif kind == "final":
+        st.raw("s_waitcnt vmcnt(0)")
+    else:
+        none, done = f"FK_VM0{name}_%=", f"FK_VMD{name}_%="
+        st.raw(f"s_cmp_ge_u32 s{S_J}, s{S_KEND}")
+        st.raw(f"s_cbranch_scc1 {none}")
+        st.raw(f"s_waitcnt vmcnt({NLOAD})")
+        st.raw(f"s_branch {done}")
+        st.label(none)
+        st.raw("s_waitcnt vmcnt(0)")
+        st.label(done)
     st.raw("s_barrier")
 
 
@@ -377,13 +508,15 @@ def entry(out):
     """Query tile 0: its first half's L/D and S/dP products (dK/dV
     accumulators cleared beside them), that half's mask when the tile needs
     one, its vector work beside the second half's S/dP products and L/D
-    reads, then a 4-way branch to the body of the first step."""
+    reads and the reads of the first step's first gradient products."""
     st = Stream(out)
     st.raw("s_nop 4")
     lds = LdsCounter()
     zero = [Ins(f"v_accvgpr_write_b32 {a(DK_BASE + i)}, 0", "accw", [a(DK_BASE + i)])
             for i in range(128)]
-    products(st, lds, (0, 0, 0), None, (0, 0, 0), zero)
+    u1, u2 = units_of((0, 0, 0), None), units_of((0, 1, 1), None)
+    products(st, lds, u1, (0, 0, 0), zero, nxt=(LEAD, u2))
+    wait_lv(st, lds, (0, 0, 0))
     st.raw("s_nop 7", 8)
     st.raw("s_nop 7", 8)
     st.raw("s_nop 3", 4)
@@ -394,7 +527,8 @@ def entry(out):
     for ins in mask_ops(0, 0):
         st.emit(ins)
     st.label(skip)
-    products(st, lds, (0, 1, 1), None, (0, 1, 1), elem_half(0))
+    products(st, lds, u2, (0, 1, 1), elem_half(0), pre=LEAD, nxt=(PRE, units_of(None, (0, 0, 0))))
+    end_step(st, lds, False)
 
 
 def generate():

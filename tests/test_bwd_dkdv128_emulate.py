@@ -42,13 +42,13 @@ def item_shape(N, k0, causal):
 
 
 def expected_bodies(N, k0, causal):
-    """Straight body while tiles j and j + 1 need no mask and tile j + 2
+    """Straight body while tiles j and j + 1 need no mask and tile j + 3
     loads whole; the masked body when either needs a mask; the general one
     otherwise; the final one last."""
     nt, ts, cnt, ragged, mlo, mhi = item_shape(N, k0, causal)
     out = []
     for j in range(cnt - 1):
-        if mlo <= j < mhi - 2:
+        if mlo <= j < mhi - 3:
             out.append("BODY")
         elif j < mlo or j + 1 >= mhi:
             out.append("ITM")
@@ -88,7 +88,7 @@ def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
         rows = np.minimum(t * BQ + np.arange(64), N - 1)
         lds[byte:byte + 256] = np.asarray(vec, np.float32)[rows].view(np.uint8)
 
-    for s in range(min(2, cnt)):
+    for s in range(min(3, cnt)):
         stage_tile(qb, ts + s, G.Q_STAGE * s)
         stage_tile(ob, ts + s, G.O_STAGE0 + G.Q_STAGE * s)
         for w in range(4):
@@ -135,21 +135,21 @@ def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
             m.v[G.TA, lane] = np.uint32((base - 4 * h - BQ * ts) & 0xFFFFFFFF)
             m.v[G.RANGE, lane] = max(N - base, 0)
         m.v[G.NINF] = np.full(64, -np.inf, np.float32).view(np.uint32)
-        for reg, addr in ((G.S_QPTR, QBASE + 2 * TILE * (ts + 2)),
-                          (G.S_OPTR, OBASE + 2 * TILE * (ts + 2)),
-                          (G.S_LPTR, LBASE + 4 * BQ * (ts + 2)),
-                          (G.S_DPTR, DBASE + 4 * BQ * (ts + 2) - 256)):
+        for reg, addr in ((G.S_QPTR, QBASE + 2 * TILE * (ts + 3)),
+                          (G.S_OPTR, OBASE + 2 * TILE * (ts + 3)),
+                          (G.S_LPTR, LBASE + 4 * BQ * (ts + 3)),
+                          (G.S_DPTR, DBASE + 4 * BQ * (ts + 3) - 256)):
             m.s[reg], m.s[reg + 1] = addr & 0xFFFFFFFF, addr >> 32
         m.s[G.S_M0Q] = 4096 * w
         m.s[G.S_M0O] = G.O_STAGE0 + 4096 * w
         m.s[G.S_M0L] = G.L_STAGE0 + 512 * w
         m.s[G.S_C] = int(c.view(np.uint32))
         m.s[G.S_LAST] = cnt - 1
-        m.s[G.S_KEND] = max(0, cnt - 2)
-        m.s[G.S_TAILJ] = cnt - 3 if ragged and cnt >= 3 else 0xFFFFFFFF
+        m.s[G.S_KEND] = max(0, cnt - 3)
+        m.s[G.S_TAILJ] = cnt - 4 if ragged and cnt >= 4 else 0xFFFFFFFF
         m.s[G.S_MLO] = mlo
         m.s[G.S_MHI] = mhi
-        m.s[G.S_FAST] = max(0, mhi - 2)
+        m.s[G.S_FAST] = max(0, mhi - 3)
         m.s[G.S_MASK0] = 1 if (mlo > 0 or mhi == 0) else 0
         m.s[G.S_J] = 0
         waves.append(m)

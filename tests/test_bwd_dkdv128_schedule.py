@@ -127,14 +127,22 @@ def body_of(name):
     return section(BODIES[name][0], "s_barrier")
 
 
+def pre_reads(stage):
+    """The reads a tile step finds in flight when it starts: those of the
+    first gradient products of its tile (in `stage`), issued by the step
+    before it (or the entry)."""
+    return [ins.text for _, reads in G.units_of(None, (stage, 0, 0))[:G.PRE] for _, ins in reads]
+
+
 def straight_paths():
+    """(lines, reads in flight at the start, p of the body or None)."""
     paths = []
     entry = LINES[:LINES.index("FK_L0_%=:")]
     i, j = entry.index("s_cbranch_scc1 FK_EMASK_%="), entry.index("FK_EMASK_%=:")
-    paths += [entry, entry[:i] + entry[j:]]
-    for name, (_, _, cases) in BODIES.items():
+    paths += [(entry, [], None), (entry[:i] + entry[j:], [], None)]
+    for name, (_, p, cases) in BODIES.items():
         for case in cases:
-            paths.append(follow(body_of(name), env_of(case)))
+            paths.append((follow(body_of(name), env_of(case)), pre_reads(p % 4), name))
     return paths
 
 
@@ -143,8 +151,9 @@ PATHS = straight_paths()
 
 @pytest.mark.parametrize("path", range(len(PATHS)))
 def test_lds_operands_landed_and_rings_not_overwritten_in_flight(path):
-    pending, last_use, n_mfma = [], {}, 0
-    for l in PATHS[path]:
+    lines, pre, _ = PATHS[path]
+    pending, last_use, n_mfma = [set(regs(split(l)[1][0])) for l in pre], {}, 0
+    for l in lines:
         op, args = split(l)
         if op == "s_waitcnt" and "lgkmcnt" in l:
             k = int(re.search(r"lgkmcnt\((\d+)\)", l).group(1))
@@ -185,7 +194,7 @@ def test_matrix_vector_hazards(path):
     product read >= 2, exponential -> use >= 1, compare -> mask read >= 2,
     product reading a register as A/B -> vector write of it >= 8."""
     t, last, src_read = 0, {}, {}
-    for l in PATHS[path]:
+    for l in PATHS[path][0]:
         op, args = split(l)
         kind = ("mfma" if op.startswith("v_mfma") else "trans" if op.startswith("v_exp") else
                 "lds" if op.startswith("ds_") else "valu" if op.startswith("v_") else "other")
@@ -232,18 +241,46 @@ def test_matrix_vector_hazards(path):
 
 
 def test_every_barrier_follows_the_lds_reads_and_the_direct_loads():
+    """Before each barrier every direct load has landed, and every LDS read
+    but the last 2 PRE (the next step's first operands, of a tile already
+    published) has returned: the L/D values the next step's vector work
+    reads among them."""
     entry = LINES[:LINES.index("FK_L0_%=:")]
     assert not any(x.startswith("global_load_lds") or x == "s_barrier" for x in entry)
+    npre = len(pre_reads(0))
+    assert entry[-1] == f"s_waitcnt lgkmcnt({npre})"
     for i, l in enumerate(LINES):
         if l == "s_barrier":
-            assert LINES[i - 1] == "s_waitcnt vmcnt(0)", i
-            assert LINES[i - 2] == "s_waitcnt lgkmcnt(0)", i
+            k = i - 1
+            while (LINES[k].endswith(":") or LINES[k].startswith("s_waitcnt vmcnt")
+                   or LINES[k].split()[0] in ("s_branch", "s_cbranch_scc1", "s_cmp_ge_u32")):
+                k -= 1
+            assert LINES[k] in (f"s_waitcnt lgkmcnt({npre})", "s_waitcnt lgkmcnt(0)"), i
+            assert LINES[i - 1].startswith("s_waitcnt vmcnt") or LINES[i - 1].startswith("FK_VMD"), i
+
+
+@pytest.mark.parametrize("path", range(len(PATHS)))
+def test_each_step_issues_the_reads_the_next_one_expects(path):
+    """A tile step that is not the last (and the entry) ends with the reads
+    of the next step's first gradient products, from the next tile's stage,
+    as its last LDS reads, and waits for all reads before them; the final
+    step leaves none in flight."""
+    lines, _, name = PATHS[path]
+    reads = [l for l in lines if l.startswith("ds_read")]
+    npre = len(pre_reads(0))
+    if name is not None and name.startswith("N"):
+        assert lines[-2:] == ["s_waitcnt lgkmcnt(0)", "s_waitcnt vmcnt(0)"]
+        return
+    stage = 0 if name is None else (BODIES[name][1] + 1) % 4
+    assert reads[-npre:] == pre_reads(stage)
+    tail = lines[len(lines) - lines[::-1].index(reads[-npre]) - 1:]
+    assert f"s_waitcnt lgkmcnt({npre})" in tail
 
 
 @pytest.mark.parametrize("path", range(len(PATHS)))
 def test_m0_set_at_least_one_state_before_each_direct_load(path):
     last_m0 = None
-    for i, l in enumerate(PATHS[path]):
+    for i, l in enumerate(PATHS[path][0]):
         if l.startswith("s_add_u32 m0,"):
             last_m0 = i
         elif l.startswith("global_load_lds"):
@@ -273,7 +310,7 @@ def tail_goff(N, tlast):
 
 @pytest.mark.parametrize("name,case", [(n, c) for n, (_, _, cs) in BODIES.items() for c in cs])
 def test_direct_loads_place_tiles_as_the_reads_expect(name, case):
-    """Tile j + 2 lands in Q, dO and L/D stage (j + 2) % 4: chunk q of row r
+    """Tile j + 3 lands in Q, dO and L/D stage (j + 3) % 4: chunk q of row r
     at slot q ^ swz(r) for all four waves, and the tile's 64 L and D values
     in each wave's own area; a partial last tile (37 rows here) through the
     clamped offsets; nothing past the end, nothing in the final step."""
@@ -325,7 +362,7 @@ def test_direct_loads_place_tiles_as_the_reads_expect(name, case):
                     lds4[dst // 4] = vec[src // 4]
                 loaded.add(("L" if is_l else "D", (m0 - G.L_STAGE0 - 512 * w) // G.LD_STAGE, clamped))
     final = name.startswith("N")
-    st = (p + 2) % 4
+    st = (p + 3) % 4
     want = set() if final or case == "skip" else {(x, st, case == "tail") for x in "QOLD"}
     assert loaded == want
     for which, stage, clamped in loaded:
@@ -347,6 +384,10 @@ def test_direct_loads_place_tiles_as_the_reads_expect(name, case):
     assert (lds4 >= 0).sum() == sum(x in "LD" for x, _, _ in loaded) * 4 * 64
 
 
+def pend_loads(pend):
+    return [(t, None, None) for t in pend]
+
+
 def run_control(N, k0, causal):
     """Execute the scalar part of the statement with the kernel's start
     values: query tiles loaded (relative index, stages, clamped), halves
@@ -360,18 +401,21 @@ def run_control(N, k0, causal):
     mhi = cnt - 1 if ragged else cnt
     TB, VB = 64 * 256, 64 * 4
     QB, OB, LB, DB = 1 << 40, 2 << 40, 3 << 40, 4 << 40
-    s = {G.S_LAST: cnt - 1, G.S_KEND: max(0, cnt - 2),
-         G.S_TAILJ: cnt - 3 if ragged and cnt >= 3 else NONE, G.S_MLO: mlo, G.S_MHI: mhi,
-         G.S_FAST: max(0, mhi - 2), G.S_J: 0, G.S_MASK0: 1 if (mlo > 0 or mhi == 0) else 0}
-    ptr = {G.S_QPTR: QB + (ts + 2) * TB, G.S_OPTR: OB + (ts + 2) * TB,
-           G.S_LPTR: LB + (ts + 2) * VB, G.S_DPTR: DB + (ts + 2) * VB - 256}
+    s = {G.S_LAST: cnt - 1, G.S_KEND: max(0, cnt - 3),
+         G.S_TAILJ: cnt - 4 if ragged and cnt >= 4 else NONE, G.S_MLO: mlo, G.S_MHI: mhi,
+         G.S_FAST: max(0, mhi - 3), G.S_J: 0, G.S_MASK0: 1 if (mlo > 0 or mhi == 0) else 0}
+    ptr = {G.S_QPTR: QB + (ts + 3) * TB, G.S_OPTR: OB + (ts + 3) * TB,
+           G.S_LPTR: LB + (ts + 3) * VB, G.S_DPTR: DB + (ts + 3) * VB - 256}
     bases = {G.S_QPTR: (QB, TB, 0), G.S_OPTR: (OB, TB, 0), G.S_LPTR: (LB, VB, 0),
              G.S_DPTR: (DB, VB, 256)}
     stage_of = {f"s{G.S_M0Q}": lambda o: o // 16384, f"s{G.S_M0O}": lambda o: o // 16384,
                 f"s{G.S_M0L}": lambda o: o // G.LD_STAGE}
-    loads = [(t, (t, t, t, t), t * 64 + 63 >= N - ts * 64) for t in range(min(2, cnt))]
+    loads = [(t, (t, t, t, t), t * 64 + 63 >= N - ts * 64) for t in range(min(3, cnt))]
     pend = {}
+    vm_out = []          # tile of each direct load in flight, in issue order
+    published = set(range(min(3, cnt)))   # the C++ prologue's, behind its barrier
     masked, bodies = [], []
+    step = None
     labels = {l[:-1]: i for i, l in enumerate(LINES) if l.endswith(":")}
     pc, scc, m0, steps = 0, None, None, 0
     while True:
@@ -385,6 +429,9 @@ def run_control(N, k0, causal):
             if l.startswith(kind) and l.endswith(":"):
                 bodies.append(kind[3:])
                 j = s[G.S_J]
+                # the step reads tiles j and j + 1: both published
+                assert {j, j + 1} & set(range(cnt)) <= published, (N, k0, j, published)
+                step = j
                 if kind == "FK_ITM":
                     masked += [(j, 1), (j + 1, 0)]
                 if kind == "FK_FIN":
@@ -413,6 +460,14 @@ def run_control(N, k0, causal):
             s[int(args[0][1:])] = int(args[1], 0)
         elif op == "s_addc_u32":
             pass
+        elif op == "s_waitcnt" and args[0].startswith("vmcnt"):
+            n = int(args[0][6:-1])
+            vm_out = vm_out[len(vm_out) - n:] if n else []
+        elif op == "s_barrier":
+            loaded = {t for t, _, _ in pend_loads(pend)} | set(range(min(3, cnt)))
+            published |= loaded - set(vm_out)
+            # the next step reads tile step + 2: it must be published now
+            assert step + 2 >= cnt or step + 2 in published, (N, k0, step, vm_out)
         elif op.startswith("global_load_lds"):
             reg = int(args[0][1:])
             key = int(args[1][2:].split(":")[0])
@@ -424,6 +479,7 @@ def run_control(N, k0, causal):
             t = (ptr[key] + extra - base) // size - ts
             assert 0 <= t < cnt, (N, k0, t)
             clamped = reg in (G.GOFF_TAIL, G.LOFF_TAIL)
+            vm_out += [t] * (4 if op == "global_load_lds_dwordx4" else 1)
             pend.setdefault(t, []).append((key, stage_of[m0[0]](m0[1] + (off if key == G.S_DPTR else 0)
                                                                     - (256 if key == G.S_DPTR else 0)),
                                            clamped))
@@ -453,7 +509,7 @@ def test_loop_loads_and_masks(N, causal):
         mhi = cnt - 1 if N % 64 else cnt
         want = []
         for j in range(cnt - 1):
-            if mlo <= j < mhi - 2:
+            if mlo <= j < mhi - 3:
                 want.append("BODY")
             elif j < mlo or j + 1 >= mhi:
                 want.append("ITM")
@@ -461,4 +517,4 @@ def test_loop_loads_and_masks(N, causal):
                 want.append("GB")
         assert bodies == want + ["FIN"], (N, k0, bodies, want)
         # the straight body is taken for every step it can take
-        assert bodies.count("BODY") == max(0, mhi - 2 - mlo)
+        assert bodies.count("BODY") == max(0, mhi - 3 - mlo)
