@@ -18,7 +18,7 @@
 // both passes: the dQ pass walks its mask row, the dK/dV pass its mask column.
 //
 // Three launches on the caller's stream, deterministic (no atomics):
-//   1. bwd_delta: D_i = dO_i . O_i and LSE_i * log2(e) (fp32), into the
+//   1. bwd_delta: -D_i = -(dO_i . O_i) and LSE_i * log2(e) (fp32), into the
 //      caller's workspace;
 //   2. bwd_dkdv:  one workgroup per 128 keys loops over 64-query tiles of Q
 //      and dO staged in LDS: S = Q K^T and
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a, long lon
 #pragma unroll
   for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
   if (row < rows && ch == 0) {
-    a.delta[row] = acc;
+    a.delta[row] = -acc;   // negated: the d = 128 dK/dV loop starts its dP products from it
     a.lse2[row] = a.lse[row] * kLog2e;  // the dK/dV and dQ passes' exponent offset
   }
 }
@@ -267,7 +267,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
               if (q >= N || (CAUSAL && key > q)) p = 0.f;
             }
             s[r] = p;
-            dp[r] = p * (dp[r] - d4[e]);
+            dp[r] = p * (dp[r] + d4[e]);
           }
         }
       };
@@ -586,7 +586,7 @@ void bwd_dkdv_split_kernel(BwdArgs a) {
               if (q >= N || (CAUSAL && key > q)) p = 0.f;
             }
             s[r] = p;
-            dp[r] = p * (dp[r] - d4[e]);
+            dp[r] = p * (dp[r] + d4[e]);
           }
         }
       };
@@ -864,7 +864,7 @@ void bwd_dq_kernel(BwdArgs a) {
             const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
             if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
           }
-          dp[r] = p * (dp[r] - dlt);
+          dp[r] = p * (dp[r] + dlt);
         }
       };
       if (need_mask) grads(std::true_type{});

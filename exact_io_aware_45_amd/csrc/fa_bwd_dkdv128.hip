@@ -8,7 +8,8 @@
 //   dV = sum_i P_i^T dO_i,  dK = scale * sum_i dS_i^T Q_i,
 //   dS = P (dP - D),  P = exp2(S c - L),
 // with S = Q K^T, dP = dO V^T, L = LSE log2(e), c = scale log2(e) and
-// D = rowsum(dO o O) from the delta pass.
+// D = rowsum(dO o O), which the delta pass stores negated (-D starts each
+// dP product chain, so the products leave dP - D).
 //
 // Work decomposition:
 //   * one workgroup = 4 waves = 128 keys of one head, one resident workgroup

@@ -6,7 +6,7 @@
 // never stored ("FlashAttention." plate, "Never write the scores"), and
 //   dQ = scale * sum_j dS_j K_j,  dS = P (dP - D),  P = exp2(S c - L),
 // with S = Q K^T, dP = dO V^T, L = LSE log2(e), c = scale log2(e) and
-// D = rowsum(dO o O) from the delta pass.
+// D = rowsum(dO o O), which the delta pass stores negated.
 //
 // Work decomposition:
 //   * one workgroup = 4 waves = 256 query rows of one head, one resident
@@ -96,7 +96,7 @@ void bwd_dq128_kernel(BwdArgs a) {
     for (int rb = 0; rb < 2; ++rb) {
       const int row = min(wrow0 + 32 * rb + l32, N - 1);
       lsel[rb] = lse2[row];
-      dd[rb] = del[row];
+      dd[rb] = del[row];   // -D
     }
     wait_vmem();   // this wave's own rows (the K tiles are published by the barrier below)
 

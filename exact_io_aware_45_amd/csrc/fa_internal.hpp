@@ -35,7 +35,7 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace: D_i = dO_i . O_i, [B][H][N] fp32
+  float* delta;  // workspace: -D_i = -(dO_i . O_i), [B][H][N] fp32
   int B, H, N, d;
   float scale;
   int causal;

@@ -19,8 +19,10 @@ gen_fwd128.py, and the half-tile pipeline the dQ loop's, gen_bwd_dq128.py):
     score products, a[192:255] four operand rings (Q rows, dO rows, Q^T and
     dO^T by transpose reads);
   * v[0:63] two slots of S and dP (lane = key, register = query) for one
-    32-query half each, v[64:95] two slots of packed P and dS, v[96:159] two
-    slots of the L and D values of the slot's 16 queries per lane half.
+    32-query half each, v[64:95] two slots of packed P and dS, v[96:127] two
+    slots of the L values of the slot's 16 queries per lane half, v[128:143]
+    the -D values that start the next dP product chain (so that it leaves
+    dP - D and the vector unit never subtracts D).
 
 Step 1 of query tile j: the exponentials and dS of (j, second half) beside
 the products dV/dK of (j, first half) and S/dP of (j + 1, first half); step 2:
@@ -58,7 +60,8 @@ QT_BASE = 224     # a[224:239] Q^T operand ring (two transpose reads per slot)
 OT_BASE = 240     # a[240:255] dO^T operand ring
 SP_BASE = 0       # v[0:63]    slot x: S[x] = v[32 x : +16], dP[x] = v[32 x + 16 : +16]
 PS_BASE = 64      # v[64:95]   slot x: P[x][cc] = v[64 + 16 x + 4 cc : +4], dS[x][cc] = +8
-LV_BASE = 96      # v[96:159]  slot x: L[x] = v[96 + 32 x : +16], D[x] = v[96 + 32 x + 16 : +16]
+LV_BASE = 96      # v[96:127]  slot x: L[x] = v[96 + 16 x : +16]
+DB_BASE = 128     # v[128:143] -D of the half whose dP products come next (their C input)
 RADDR = 160       # v[160:167] Q row-read addresses per d chunk c (stage 0, half 0)
 DRADDR = 168      # v[168:175] dO row-read addresses
 TADDR = 176       # v[176:183] Q^T transpose-read addresses, index 2 db + hi
@@ -122,11 +125,7 @@ def ds_reg(x, cc):
 
 
 def l_reg(x, r):
-    return LV_BASE + 32 * x + r
-
-
-def d_reg(x, r):
-    return LV_BASE + 32 * x + 16 + r
+    return LV_BASE + 16 * x + r
 
 
 # --------------------------------------------------------------- operands
@@ -152,26 +151,40 @@ def tr_reads(which, o, stage, half):
 
 
 def lv_reads(stage, half, x):
-    """L and D of query half `half` into slot x: register 4g + e holds query
-    32 half + 8 g + 4 h + e."""
+    """L of query half `half` into slot x: register 4g + e holds query
+    32 half + 8 g + 4 h + e (the row of the score products' results)."""
     out = []
-    for which, reg, extra in (("L", l_reg, 0), ("D", d_reg, 256)):
-        for g in range(4):
-            off = LD_STAGE * stage + 4 * (32 * half + 8 * g) + extra
-            out.append(((which, g), Ins(f"ds_read_b128 {vr(reg(x, 4 * g), 4)}, {v(LADDR)} offset:{off}",
-                                       "lds", regs_v(reg(x, 4 * g), 4), [v(LADDR)])))
+    for g in range(4):
+        off = LD_STAGE * stage + 4 * (32 * half + 8 * g)
+        out.append((("L", g), Ins(f"ds_read_b128 {vr(l_reg(x, 4 * g), 4)}, {v(LADDR)} offset:{off}",
+                                  "lds", regs_v(l_reg(x, 4 * g), 4), [v(LADDR)])))
+    return out
+
+
+def d_reads(stage, half):
+    """-D of query half `half` (the delta pass stores it negated) into the
+    C input of the half's first dP product, laid out as its results, so that
+    the products leave dP - D."""
+    out = []
+    for g in range(4):
+        off = LD_STAGE * stage + 4 * (32 * half + 8 * g) + 256
+        out.append((("D", g), Ins(f"ds_read_b128 {vr(DB_BASE + 4 * g, 4)}, {v(LADDR)} offset:{off}",
+                                  "lds", regs_v(DB_BASE + 4 * g, 4), [v(LADDR)])))
     return out
 
 
 def sdp_mfma(which, c, dst):
-    """S (which = "Q") or dP (which = "O") product of d chunk c into slot dst."""
+    """S (which = "Q") or dP (which = "O") product of d chunk c into slot
+    dst; the dP chain starts from -D (DB_BASE), the S chain from 0."""
     d0 = s_reg(dst, 0) if which == "Q" else dp_reg(dst, 0)
     ring = QR_BASE if which == "Q" else OR_BASE
     slot = ring + 4 * (c % RING)
     b = (KB_BASE if which == "Q" else VB_BASE) + 4 * c
-    src_c = "0" if c == 0 else vr(d0, 16)
+    cin = d0 if c else (DB_BASE if which == "O" else None)
+    src_c = "0" if cin is None else vr(cin, 16)
     return Ins(f"v_mfma_f32_32x32x16_bf16 {vr(d0, 16)}, {ar(slot, 4)}, {ar(b, 4)}, {src_c}",
-               "mfma", regs_v(d0, 16), regs_a(slot, 4) + regs_a(b, 4), regs_v(d0, 16) if c else [])
+               "mfma", regs_v(d0, 16), regs_a(slot, 4) + regs_a(b, 4),
+               regs_v(cin, 16) if cin is not None else [])
 
 
 def grad_mfma(which, o, src):
@@ -213,8 +226,9 @@ def mask_ops(x, half):
 
 
 def elem_half(x):
-    """P = exp2(S c - L), dS = P (dP - D) for slot x, in place, P and dS
-    packed to bf16 pairs; software-pipelined over groups of four elements."""
+    """P = exp2(S c - L), dS = P (dP - D) for slot x (the products leave
+    dP - D), in place, P and dS packed to bf16 pairs; software-pipelined over
+    groups of four elements."""
     groups = []
     for g in range(4):
         rs = list(range(4 * g, 4 * g + 4))
@@ -222,8 +236,6 @@ def elem_half(x):
                    "valu", [v(s_reg(x, r))], [v(s_reg(x, r)), v(l_reg(x, r))]) for r in rs]
         ex = [Ins(f"v_exp_f32 {v(s_reg(x, r))}, {v(s_reg(x, r))}", "trans", [v(s_reg(x, r))],
                   [v(s_reg(x, r))]) for r in rs]
-        ex += [Ins(f"v_sub_f32 {v(dp_reg(x, r))}, {v(dp_reg(x, r))}, {v(d_reg(x, r))}", "valu",
-                   [v(dp_reg(x, r))], [v(dp_reg(x, r)), v(d_reg(x, r))]) for r in rs]
         fin = [Ins(f"v_mul_f32 {v(dp_reg(x, r))}, {v(s_reg(x, r))}, {v(dp_reg(x, r))}", "valu",
                    [v(dp_reg(x, r))], [v(s_reg(x, r)), v(dp_reg(x, r))]) for r in rs]
         for r in (4 * g, 4 * g + 2):
@@ -266,8 +278,9 @@ def units_of(sdp, grad):
     if sdp:
         s_stg, s_half, dst = sdp
         for i in range(8):
+            dreads = d_reads(s_stg, s_half) if i == 0 else []
             sd.append([(sdp_mfma("Q", i, dst), [(("Q", i), row_read("Q", i, s_stg, s_half))]),
-                       (sdp_mfma("O", i, dst), [(("O", i), row_read("O", i, s_stg, s_half))])])
+                       (sdp_mfma("O", i, dst), dreads + [(("O", i), row_read("O", i, s_stg, s_half))])])
     if not g or not sd:
         return [u for pair in g + sd for u in pair]
     order = g[:1]
@@ -573,7 +586,7 @@ def generate():
 
 
 def clobbers():
-    regs = [f"v{i}" for i in range(0, LV_BASE + 64)]   # S/dP, P/dS, L/D slots
+    regs = [f"v{i}" for i in range(0, LV_BASE + 64)]   # S/dP, P/dS, L slots, -D, v[144:159]
     regs += [f"v{i}" for i in range(TMP, TMP + 8)]
     regs += [f"a{i}" for i in range(QR_BASE, 256)]     # operand rings
     regs += [f"s{i}" for i in range(S_T, S_T + 9)]

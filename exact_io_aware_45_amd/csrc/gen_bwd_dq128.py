@@ -58,7 +58,7 @@ TR_BASE = 192     # v[192:207] K^T operand ring (two transpose reads per slot)
 RADDR = 208       # v[208:215] row-read addresses per d chunk c (K stage 0, key block 0)
 TADDR = 216       # v[216:223] transpose-read addresses (K stage 0), index 2 db + hi
 LSEL = 224        # v224, v225: L = LSE log2(e) per row block
-DDEL = 226        # v226, v227: D per row block
+DDEL = 226        # v226, v227: -D per row block (the delta pass stores D negated)
 GOFF = 228        # v[228:231] direct-load offsets within a tile (whole tiles)
 GOFF_TAIL = 232   # v[232:235] direct-load offsets of the partial last tile
 THR = 236         # v236, v237: mask threshold of the tile masked in step 2
@@ -225,7 +225,7 @@ def elem_half(kb):
                for rb, r in elems]
         ex = [Ins(f"v_exp_f32 {v(s_reg(kb, rb, r))}, {v(s_reg(kb, rb, r))}", "trans",
                   [v(s_reg(kb, rb, r))], [v(s_reg(kb, rb, r))]) for rb, r in elems]
-        ex += [Ins(f"v_sub_f32 {v(dp_reg(kb, rb, r))}, {v(dp_reg(kb, rb, r))}, {v(DDEL + rb)}", "valu",
+        ex += [Ins(f"v_add_f32 {v(dp_reg(kb, rb, r))}, {v(dp_reg(kb, rb, r))}, {v(DDEL + rb)}", "valu",
                    [v(dp_reg(kb, rb, r))], [v(dp_reg(kb, rb, r)), v(DDEL + rb)]) for rb, r in elems]
         fin = [Ins(f"v_mul_f32 {v(s_reg(kb, rb, r))}, {v(s_reg(kb, rb, r))}, {v(dp_reg(kb, rb, r))}",
                    "valu", [v(s_reg(kb, rb, r))], [v(s_reg(kb, rb, r)), v(dp_reg(kb, rb, r))])

@@ -76,7 +76,7 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 
 /*
  * Bytes of device workspace fa_backward needs for this shape: two fp32
- * [B][H][N] arrays, the per-row D_i = dO_i . O_i and LSE_i * log2(e), which
+ * [B][H][N] arrays, the per-row -D_i = -(dO_i . O_i) and LSE_i * log2(e), which
  * the first launch writes and the other two read.  Returns 0 for empty or
  * invalid shapes.
  */

@@ -4,8 +4,8 @@ The instruction text that gen_bwd_dkdv128.py emits (fa_bwd_dkdv128_loop.inc)
 is executed for the four waves of one workgroup by the emulator in _emu.py.
 The setup (registers, and the Q, dO tiles and L, D values staged before the
 loop) restates the C++ of fa_bwd_dkdv128.hip; L = LSE log2(e) and D come from
-the oracle's forward statistics, rounded to fp32 as the delta pass stores
-them.  dK is scaled as the kernel's epilogue does; dK and dV are compared
+the oracle's forward statistics, rounded to fp32 and (D) negated as the delta
+pass stores them.  dK is scaled as the kernel's epilogue does; dK and dV are compared
 with the fp64 oracle at the bf16 tolerances, and the sequence of loop bodies
 each query tile step takes is checked against the rule that selects them.
 """
@@ -64,7 +64,7 @@ def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
     qb = bf16_bits(q).astype(np.uint16).reshape(-1).view(np.uint8).copy()
     ob = bf16_bits(do).astype(np.uint16).reshape(-1).view(np.uint8).copy()
     lb = np.asarray(lse2, np.float32).view(np.uint8).copy()
-    db_ = np.asarray(delta, np.float32).view(np.uint8).copy()
+    db_ = np.asarray(-delta, np.float32).view(np.uint8).copy()   # the delta pass stores -D
     mem = Memory([(QBASE, qb), (OBASE, ob), (LBASE, lb), (DBASE, db_)])
     lds = np.zeros(139264, np.uint8)
     TILE = BQ * D
@@ -93,7 +93,7 @@ def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
         stage_tile(ob, ts + s, G.O_STAGE0 + G.Q_STAGE * s)
         for w in range(4):
             stage_vec(lse2, ts + s, G.L_STAGE0 + G.LD_STAGE * s + 512 * w)
-            stage_vec(delta, ts + s, G.L_STAGE0 + G.LD_STAGE * s + 512 * w + 256)
+            stage_vec(-delta, ts + s, G.L_STAGE0 + G.LD_STAGE * s + 512 * w + 256)
     waves = []
     for w in range(4):
         m = Machine()

@@ -167,7 +167,7 @@ def test_lds_operands_landed_and_rings_not_overwritten_in_flight(path):
             pending.append(dst)
             assert len(pending) <= 15, ("more LDS reads in flight than lgkmcnt can count", l)
         elif op.startswith("v_mfma"):
-            srcs = set(regs(args[1])) | set(regs(args[2]))
+            srcs = set(regs(args[1])) | set(regs(args[2])) | set(regs(args[3]))
             for p in pending:
                 assert not (p & srcs), ("operand not landed", l)
             n_mfma += 1

@@ -4,7 +4,8 @@ The instruction text that gen_bwd_dq128.py emits (fa_bwd_dq128_loop.inc) is
 executed for the four waves of one workgroup by the emulator in _emu.py.
 The setup (registers, and K, V tiles 0 and 1 staged before the loop)
 restates the C++ of fa_bwd_dq128.hip; L = LSE log2(e) and D come from the
-oracle's forward statistics, rounded to fp32 as the delta pass stores them.
+oracle's forward statistics, rounded to fp32 and (D) negated as the delta
+pass stores them.
 dQ is scaled as the kernel's epilogue does and compared with the fp64
 oracle at the bf16 tolerances; the sequence of loop bodies each tile step
 takes is checked against the rule that selects them.
@@ -102,7 +103,7 @@ def emulate_dq(q, k, v, do, lse2, delta, N, q0, causal, scale):
                         for t in range(4):
                             m.a[base + 32 * rb + 4 * cc + t, lane] = e[2 * t] | (e[2 * t + 1] << 16)
                 m.v[G.LSEL + rb, lane] = np.float32(lse2[r]).view(np.uint32)
-                m.v[G.DDEL + rb, lane] = np.float32(delta[r]).view(np.uint32)
+                m.v[G.DDEL + rb, lane] = np.float32(-delta[r]).view(np.uint32)   # stored negated
                 row = wrow0 + 32 * rb + l32
                 lim = min(row, N - 1) if causal else N - 1
                 m.v[G.THR1 + rb, lane] = np.uint32((lim - 4 * h - BC * f) & 0xFFFFFFFF)
