@@ -20,7 +20,7 @@
 //     gen_bwd_dq128.py) that overlaps each 32-key half's exponentials and dS
 //     with the products of its neighbours.  The C++ below stages the item's
 //     Q and dO rows through LDS into registers, sets up addresses, and stores
-//     dQ.
+//     dQ through LDS in whole rows while the next item's first loads land.
 #include "fa_bwd_dq128_loop.inc"
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
@@ -48,7 +48,8 @@ void bwd_dq128_kernel(BwdArgs a) {
   // LDS, bytes: [0, 64K) K stages 0-3 and [64K, 96K) V stages 0-1 (the
   // generated loop addresses these directly); [96K, 160K) each wave's 64
   // query rows at the start of an item.  An item's dO rows pass through
-  // [32K, 96K) before its first V tiles load there.
+  // [32K, 96K) before its first V tiles load there.  After the loop,
+  // [32K w, 32K (w + 1)) stages wave w's dQ rows.
   __shared__ __attribute__((aligned(1024))) bf16 smem[10 * TILE];
   constexpr uint32_t VST0 = 4 * TILE_BYTES, QST0 = 6 * TILE_BYTES, DOST0 = 2 * TILE_BYTES;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -56,32 +57,49 @@ void bwd_dq128_kernel(BwdArgs a) {
     return fresh(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem)));
   };
 
+  auto shape = [&]() { return fresh_shape<BR, BC>(a.N, a.B, a.H, a.Hkv); };
+  auto tend_of = [&](const Shape& sh, const Item& it) {
+    return CAUSAL ? min(sh.nt, (min(it.q0 + BR, sh.N) - 1) / BC + 1) : sh.nt;
+  };
+  // An item's first loads: this wave's Q and dO rows and K tiles 0 and 1
+  // (the LDS they fill is free: the previous item's loop and epilogue ended
+  // with a barrier after their last read).
+  auto dma_first = [&](const Shape& sh, const Item& it) {
+    const int wave = fresh(wave0);
+    const uint32_t lds0 = lds_base();
+    const size_t head = (size_t)it.bh * (size_t)sh.N * D;
+    const bf16* K = fresh(reinterpret_cast<const bf16*>(a.k)) + kv_head_offset(sh, it.bh, D);
+    dma_rows128(sh, fresh(reinterpret_cast<const bf16*>(a.q)) + head, it.q0 + 64 * wave,
+                lds0 + QST0 + 16384u * wave);
+    dma_rows128(sh, fresh(reinterpret_cast<const bf16*>(a.dout)) + head, it.q0 + 64 * wave,
+                lds0 + DOST0 + 16384u * wave);
+    dma_tile128(sh, wave, K, 0, lds0);
+    if (tend_of(sh, it) > 1) dma_tile128(sh, wave, K, 1, lds0 + TILE_BYTES);
+  };
+
+  Item cur;
+  {
+    const Shape sh = shape();
+    if (!resident_item<CAUSAL, BR>(sh, 0, cur)) return;
+    dma_first(sh, cur);
+  }
+
   for (int r = 0;; ++r) {
-    const Shape sh = fresh_shape<BR, BC>(a.N, a.B, a.H, a.Hkv);
-    Item cur;
-    if (!resident_item<CAUSAL, BR>(sh, r, cur)) break;
+    const Shape sh = shape();
+    Item nxt;
+    const bool more = resident_item<CAUSAL, BR>(sh, r + 1, nxt);
     const int N = sh.N, nt = sh.nt;
     const int wave = fresh(wave0);
     const uint32_t lds0 = lds_base();
     const int q0 = cur.q0;
     const int wrow0 = q0 + 64 * wave;
-    const size_t head = (size_t)cur.bh * (size_t)N * D;
     const size_t kv = kv_head_offset(sh, cur.bh, D);
     const bf16* __restrict__ K = fresh(reinterpret_cast<const bf16*>(a.k)) + kv;
     const bf16* __restrict__ V = fresh(reinterpret_cast<const bf16*>(a.v)) + kv;
-    const int tend = CAUSAL ? min(nt, (min(q0 + BR, N) - 1) / BC + 1) : nt;
+    const int tend = tend_of(sh, cur);
     int fm = tend;
     if (CAUSAL) fm = min(fm, q0 / BC);
     if (sh.ragged) fm = min(fm, nt - 1);
-
-    // This wave's Q and dO rows and K tiles 0 and 1 (the previous item's loop
-    // ended with a barrier, so every LDS area is free).
-    dma_rows128(sh, fresh(reinterpret_cast<const bf16*>(a.q)) + head, wrow0,
-                lds0 + QST0 + 16384u * wave);
-    dma_rows128(sh, fresh(reinterpret_cast<const bf16*>(a.dout)) + head, wrow0,
-                lds0 + DOST0 + 16384u * wave);
-    dma_tile128(sh, wave, K, 0, lds0);
-    if (tend > 1) dma_tile128(sh, wave, K, 1, lds0 + TILE_BYTES);
 
     const int lane = fresh_lane();
     const int h = lane >> 5;
@@ -216,29 +234,47 @@ void bwd_dq128_kernel(BwdArgs a) {
                    "{s69}"(stailj), "{s70}"(sfm), "{s82}"(sfast)
                  : FA_BWD_DQ128_LOOP_CLOBBERS);
 
-    // dQ = scale * acc, fp32: lane (l32, h) of block (rb, db) holds
-    // d = 32 db + 8 g + 4 h .. +3 in registers 4g .. 4g + 3.
-    const Shape sh2 = fresh_shape<BR, BC>(a.N, a.B, a.H, a.Hkv);
+    // Epilogue: dQ = scale * acc, fp32.  Lane (l32, h) of block (rb, db)
+    // holds row 32 rb + l32, d = 32 db + 8 g + 4 h .. +3 in registers 4g ..
+    // 4g + 3: stored as it is, every instruction would write 32 B pieces of
+    // 32 rows.  Each wave passes its 64 rows through its own 32 KiB of LDS
+    // instead (16-byte chunk q of row k at slot q ^ (k mod 32), so that the
+    // writes of 32 rows and the reads of 2 whole rows both spread over the
+    // banks) and stores 1 KiB of two consecutive rows per instruction.
+    const Shape sh2 = shape();
+    const int wave2 = fresh(wave0);
     const int el = fresh_lane(), eh = el >> 5, e32 = el & 31;
-    const int wrow2 = cur.q0 + 64 * fresh(wave0);
     const float sc = fresh(a.scale);
-    typedef __attribute__((address_space(1))) f32x4 gf32x4;
+    FA_LDS char* stg = (FA_LDS char*)smem + 32768 * wave2;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = wrow2 + 32 * rb + e32;
-      if (row < sh2.N) {
-        gf32x4* dst = (gf32x4*)(fresh(a.dq) + ((size_t)cur.bh * sh2.N + row) * D + 4 * eh);
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 x;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = acc[rb][db][4 * g + e] * sc;
-            dst[(32 * db + 8 * g) / 4] = x;
-          }
-      }
+          for (int e = 0; e < 4; ++e) x[e] = acc[rb][db][4 * g + e] * sc;
+          *reinterpret_cast<FA_LDS f32x4*>(stg + 512 * (32 * rb + e32) +
+                                           16 * ((8 * db + 2 * g + eh) ^ e32)) = x;
+        }
+    f32x4 rq[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int row = 2 * i + eh;
+      rq[i] = *reinterpret_cast<const FA_LDS f32x4*>(stg + 512 * row + 16 * (e32 ^ (row & 31)));
     }
+    __syncthreads();   // every wave has its rows: the LDS takes the next item's first loads
+    if (more) dma_first(sh2, nxt);
+    const int wrow2 = cur.q0 + 64 * wave2;
+    typedef __attribute__((address_space(1))) f32x4 gf32x4;
+    gf32x4* dqp = (gf32x4*)(fresh(a.dq) + ((size_t)cur.bh * sh2.N + wrow2 + eh) * D + 4 * e32);
+    const int rows = sh2.N - wrow2;   // rows of this wave inside the sequence
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (2 * i + eh < rows) dqp[i * (2 * D / 4)] = rq[i];
+    if (!more) break;
+    cur = nxt;
   }
 }
 
