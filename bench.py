@@ -90,15 +90,17 @@ def traffic_bytes(w, which: str) -> float:
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd.hip", "fa_common.hpp"),
     "fwd128_kernel": ("fa_fwd128.hip", "fa_fwd128_loop.inc", "fa_resident.hpp", "fa_common.hpp"),
+    "fwd64_kernel": ("fa_fwd64.hip", "fa_fwd64_loop.inc", "fa_resident.hpp", "fa_common.hpp"),
     "fa_backward": ("fa_bwd.hip", "fa_bwd_dkdv128.hip", "fa_bwd_dkdv128_loop.inc", "fa_bwd_dq128.hip",
                     "fa_bwd_dq128_loop.inc", "fa_resident.hpp", "fa_common.hpp"),
 }
 
 
-def uses_fwd128(w) -> bool:
-    """Whether fa_forward takes the hand-scheduled d = 128 kernel: bf16, no
-    tile mask, at least 256 query tiles of 256 rows."""
-    return (w.dtype == "bf16" and w.d == 128 and not w.sparse
+def uses_resident_fwd(w) -> bool:
+    """Whether fa_forward takes the hand-scheduled kernel of its head dim
+    (fwd128_kernel, fwd64_kernel): bf16, no tile mask, at least 256 query
+    tiles of 256 rows."""
+    return (w.dtype == "bf16" and w.d in (64, 128) and not w.sparse
             and -(-w.N // 256) * w.B * w.H >= 256)
 
 
@@ -443,9 +445,9 @@ def main():
     elif w.dtype == "fp8":
         fwd_kernel = (f"fwd_fp8_kernel<d={w.d}, BC=64, {8 if w.d == 128 else 4} waves, {mode}> "
                       "(1 launch per fa_forward_fp8)")
-    elif uses_fwd128(w):
+    elif uses_resident_fwd(w):
         entry = "_gqa" if w.Hkv else ""
-        fwd_kernel = (f"fwd128_kernel<{mode}> (1 launch per fa_forward{entry}; one resident "
+        fwd_kernel = (f"fwd{w.d}_kernel<{mode}> (1 launch per fa_forward{entry}; one resident "
                       "4-wave workgroup per CU, 256-row query tiles)")
     else:
         entry = "_blocksparse" if w.sparse else ("_gqa" if w.Hkv else "")
@@ -475,7 +477,8 @@ def main():
         "fwd": {"ms": round(fwd_ms, 4), **spread(fwd_each), "tflops": round(fwd_tf, 2),
                 "frac_of_peak": round(fwd_tf / peak, 4), "flops": ff},
         "roofline": roofline(w, "fwd", fwd_ms, ff,
-                             traffic.get("fwd128_kernel" if uses_fwd128(w) else "fwd_bf16_kernel"),
+                             traffic.get(f"fwd{w.d}_kernel" if uses_resident_fwd(w)
+                                         else "fwd_bf16_kernel"),
                              fwd_kernel),
     }
     if w.Hkv:

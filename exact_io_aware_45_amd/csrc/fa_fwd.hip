@@ -382,6 +382,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   if (fwd128_applies(a)) return launch_fwd128(a, s);
+  if (fwd64_applies(a)) return launch_fwd64(a, s);
   if (a.d == 128) return launch_d<128, 64>(a, s);
   if (a.d == 64) return launch_d<64, 64>(a, s);
   return hipErrorInvalidValue;

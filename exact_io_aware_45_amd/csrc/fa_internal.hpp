@@ -55,6 +55,8 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 bool fwd128_applies(const FwdArgs& a);
 hipError_t launch_fwd128(const FwdArgs& a, hipStream_t s);
+bool fwd64_applies(const FwdArgs& a);
+hipError_t launch_fwd64(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);

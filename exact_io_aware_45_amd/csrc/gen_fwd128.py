@@ -1,8 +1,10 @@
-"""Generate the hand-scheduled main loop of the d = 128 bf16 forward kernel.
+"""Generate the hand-scheduled main loops of the d = 128 and d = 64 bf16
+forward kernels.
 
     python exact_io_aware_45_amd/csrc/gen_fwd128.py      # rewrites fa_fwd128_loop.inc
+                                                         # and fa_fwd64_loop.inc
 
-The loop runs inside fa_fwd128.hip as one inline-assembly statement; its
+The loop runs inside fa_fwd128.hip (fa_fwd64.hip) as one inline-assembly statement; its
 registers are pinned (the register map below), so the instruction order and
 the register allocation are both fixed here rather than left to the compiler,
 which serialised the three phases of a key tile (scores, softmax, P V) when it
@@ -18,10 +20,13 @@ How it is laid out is specific to gfx950:
   * one wave owns 64 query rows (two 32-row blocks) for the whole key loop,
     one wave per SIMD, so every K and V^T operand read from LDS feeds two
     matrix instructions;
-  * iteration j issues the 32 products of S_{j+1} = K_{j+1} Q^T while the
-    vector unit finishes tile j's exponentials (second 32-key half), then the
-    32 products O += V_j^T P_j^T while it starts tile j+1's exponentials
-    (first half): matrix and vector work of neighbouring tiles overlap;
+  * iteration j issues the products of S_{j+1} = K_{j+1} Q^T (32 at d = 128,
+    16 at d = 64) while the vector unit finishes tile j's exponentials
+    (second 32-key half), then those of O += V_j^T P_j^T while it starts
+    tile j+1's exponentials (first half): matrix and vector work of
+    neighbouring tiles overlap.  The vector work is the same at both head
+    dims, so at d = 64 it is the longer of the two and is spread evenly
+    over the products;
   * the exponentials use a running per-row reference m instead of each
     tile's maximum (softmax is unchanged by the reference; the final
     normalisation divides by a sum taken against the same reference).  A
@@ -48,12 +53,21 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+
+# ------------------------------------------------------------------ head dim
+# configure() sets these for one head dim (d = 128 when imported).
+D = 128           # head dim
+NC = D // 16      # 16-wide d chunks: K row operands per 32 keys, Q^T operands per row block
+NDB = D // 32     # 32-wide d blocks of O^T
+NLOAD = D // 32   # direct loads (1 KiB each) per wave per K or V tile
 OUT = os.path.join(HERE, "fa_fwd128_loop.inc")
+MACRO = "FA_FWD128_LOOP"
+KERNEL = "fwd128_kernel (fa_fwd128.hip)"
 
 # ---------------------------------------------------------------- register map
 # AGPRs
-O_BASE = 0        # a[0:127]   O^T accumulators: O[rb][db] = a[64 rb + 16 db : +16]
-Q_BASE = 128      # a[128:191] Q^T operands:     Q[rb][c]  = a[128 + 32 rb + 4 c : +4]
+O_BASE = 0        # a[0:16 NDB * 2]  O^T accumulators: O[rb][db] = a[16 NDB rb + 16 db : +16]
+Q_BASE = 128      # a[128:128 + 8 NC] Q^T operands:  Q[rb][c]  = a[128 + 4 NC rb + 4 c : +4]
 KRING = 8         # K operand ring slots (4 registers each)
 VRING = 8         # V^T operand ring slots
 KAHEAD = 3        # K operands read ahead of their first product
@@ -63,9 +77,9 @@ VR_BASE = 224     # a[224:255] V^T operand ring
 # VGPRs
 S_BASE = (0, 64)  # v[0:63], v[64:127]   scores S[rb][kb] = v[base + 32 rb + 16 kb : +16]
 P_BASE = (128, 160)  # v[128:159], v[160:191] packed weights P[rb][kb][cc] = v[base + 16 rb + 8 kb + 4 cc : +4]
-KADDR = 192       # v[192:199] K operand LDS addresses (stage 0, kb 0), one per c
-VADDR = 200       # v[200:207] V^T LDS addresses (stage 0), index 2 db + hi
-GOFF = 208        # v[208:211] per-lane byte offsets of the 4 direct loads within a tile
+KADDR = 192       # v[192:192 + NC] K operand LDS addresses (stage 0, kb 0), one per c
+VADDR = 200       # v[200:200 + 2 NDB] V^T LDS addresses (stage 0), index 2 db + hi
+GOFF = 208        # v[208:208 + NLOAD] per-lane byte offsets of the direct loads within a tile
 MNEG = 212        # v212, v213: -m (reference, log2 units) per row block
 LSUM = 214        # v214, v215: running row sums (this lane's keys) per row block
 TS = 216          # v[216:219] tile partial sums ts[rb][i] = v[216 + 2 rb + i], i = 0, 1
@@ -74,7 +88,7 @@ TMP = 225         # v[225:248] temporaries
 NTMP = 24
 THR = 249         # v249, v250: mask threshold per row block for the next masked tile
 NINF = 251        # v251: -inf
-GOFF_TAIL = 252   # v[252:255] direct-load offsets of the ragged last tile (rows clamped)
+GOFF_TAIL = 252   # v[252:252 + NLOAD] direct-load offsets of the ragged last tile (rows clamped)
 # SGPRs
 S_KPTR = 60       # s[60:61] global address of the next K tile to load
 S_VPTR = 62       # s[62:63] global address of the next V tile to load
@@ -92,16 +106,35 @@ S_MASK = (74, 76, 78, 80)   # SGPR pairs for element masks
 S_FAST = 82       # iterations j < this take the straight body: tile j + 1 needs no
                   # mask and both of its loads are whole tiles
 
-# LDS map (bytes): V stage 0 at 0, V stage 1 at 16 KiB, K stage 0 at 32 KiB,
-# K stage 1 at 48 KiB.  KADDR/VADDR hold stage-0 addresses; a stage adds 16 KiB.
-STAGE_BYTES = 16384
-TILE_BYTES = 64 * 256   # one 64-key tile of K or V in global memory
+# LDS map (bytes): V stage 0 at 0, V stage 1 at STAGE_BYTES, K stage 0 at
+# 2 STAGE_BYTES, K stage 1 at 3 STAGE_BYTES (one 64-key tile each: 16 KiB at
+# d = 128, 8 KiB at d = 64).  KADDR/VADDR hold stage-0 addresses.
+STAGE_BYTES = 64 * D * 2
+TILE_BYTES = 64 * D * 2   # one 64-key tile of K or V in global memory
 
 THRESH = "0x43800000"   # 256.0: the per-lane tile sum that sends a tile to the slow path
 
 # Conservative issue-cycle costs used to fill the shadow of each product.
 COST = {"valu": 4.5, "trans": 8.0, "accw": 4.5, "lds": 4.0, "salu": 4.0, "vmem": 4.0, "nop": 1.0}
-SLOT = 27.0   # vector/LDS issue cycles one wave can overlap with one product
+SLOT = 27.0   # vector/LDS issue cycles placed beside one product
+
+
+def configure(d):
+    """Set the module's head-dim dependent values (d = 128 or 64).  At d = 64
+    the vector work of a half-tile (the same as at d = 128) exceeds the
+    shadow of its 16 products, so the slot budget grows to spread it evenly
+    instead of leaving a tail after the last product."""
+    global D, NC, NDB, NLOAD, OUT, MACRO, KERNEL, STAGE_BYTES, TILE_BYTES, SLOT
+    assert d in (64, 128)
+    D, NC, NDB, NLOAD = d, d // 16, d // 32, d // 32
+    OUT = os.path.join(HERE, f"fa_fwd{d}_loop.inc")
+    MACRO = f"FA_FWD{d}_LOOP"
+    KERNEL = f"fwd{d}_kernel (fa_fwd{d}.hip)"
+    STAGE_BYTES = TILE_BYTES = 64 * d * 2
+    SLOT = 27.0 if d == 128 else SLOT64
+
+
+SLOT64 = 40.0
 
 # Hazard distances (in issued instructions; s_nop N counts N+1).
 H_MFMA_TO_READ = 18   # product result -> vector/LDS/accvgpr read
@@ -305,13 +338,13 @@ def full_loads(which, stage):
     """Direct HBM -> LDS loads of one whole K or V tile into `stage`: M0 is
     the wave's base in the stage and load i fills LDS [M0 + 1024 i, +1024)
     from offsets GOFF + i, which have 1024 i taken off (the instruction
-    offset is added to both addresses).  Returns (M0 set-up, the four loads,
+    offset is added to both addresses).  Returns (M0 set-up, the NLOAD loads,
     the pointer step to the next tile); M0 must be written at least one
     instruction before the first load."""
     sptr, sm0 = (S_KPTR, S_M0K) if which == "K" else (S_VPTR, S_M0V)
     pre = [f"s_add_u32 m0, s{sm0}, {STAGE_BYTES * stage}"]
     loads = [f"global_load_lds_dwordx4 {v(GOFF + i)}, s[{sptr}:{sptr + 1}] offset:{1024 * i}"
-             for i in range(4)]
+             for i in range(NLOAD)]
     post = [f"s_add_u32 s{sptr}, s{sptr}, {TILE_BYTES}", f"s_addc_u32 s{sptr + 1}, s{sptr + 1}, 0"]
     return pre, loads, post
 
@@ -321,7 +354,7 @@ def tail_loads(which, stage):
     sequence (absolute, so M0 carries the 1024 i)."""
     sptr, sm0 = (S_KPTR, S_M0K) if which == "K" else (S_VPTR, S_M0V)
     out = []
-    for i in range(4):
+    for i in range(NLOAD):
         out += [f"s_add_u32 m0, s{sm0}, {STAGE_BYTES * stage + 1024 * i}", "s_nop 0",
                 f"global_load_lds_dwordx4 {v(GOFF_TAIL + i)}, s[{sptr}:{sptr + 1}]"]
     return out
@@ -387,7 +420,7 @@ def k_read(o, stage):
     """K operand o = (c, kb) into ring slot o % KRING."""
     c, kb = o // 2, o % 2
     slot = KR_BASE + 4 * (o % KRING)
-    off = STAGE_BYTES * stage + 8192 * kb
+    off = STAGE_BYTES * stage + 32 * 2 * D * kb
     return Ins(f"ds_read_b128 {ar(slot, 4)}, {v(KADDR + c)} offset:{off}", "lds",
                regs_a(slot, 4), [v(KADDR + c)])
 
@@ -395,10 +428,10 @@ def k_read(o, stage):
 def v_reads(o, stage):
     """V^T operand o = (block b = 2 kb + cc, db): two transpose reads into
     ring slot o % VRING (rows of the block's first and second 8-key groups)."""
-    b, db = o // 4, o % 4
+    b, db = o // NDB, o % NDB
     kb, cc = b // 2, b % 2
     slot = VR_BASE + 4 * (o % VRING)
-    off = STAGE_BYTES * stage + (32 * kb + 16 * cc) * 256
+    off = STAGE_BYTES * stage + (32 * kb + 16 * cc) * 2 * D
     return [Ins(f"ds_read_b64_tr_b16 {ar(slot + 2 * hi, 2)}, {v(VADDR + 2 * db + hi)} offset:{off}",
                 "lds", regs_a(slot + 2 * hi, 2), [v(VADDR + 2 * db + hi)]) for hi in range(2)]
 
@@ -410,20 +443,20 @@ def s_mfma(m, nxt):
     dst = s_reg(nxt, rb, kb, 0)
     src_c = "0" if c == 0 else vr(dst, 16)
     slot = KR_BASE + 4 * (o % KRING)
-    q = Q_BASE + 32 * rb + 4 * c
+    q = Q_BASE + 4 * NC * rb + 4 * c
     srcc = regs_v(dst, 16) if c else []
     return Ins(f"v_mfma_f32_32x32x16_bf16 {vr(dst, 16)}, {ar(slot, 4)}, {ar(q, 4)}, {src_c}",
                "mfma", regs_v(dst, 16), regs_a(slot, 4) + regs_a(q, 4), srcc)
 
 
 def pv_mfma(m, pbuf):
-    """Product m of the P V phase: block b = m // 8 (kb = b // 2, cc = b % 2),
-    db = (m // 2) % 4, rb = m % 2."""
-    b, db, rb = m // 8, (m // 2) % 4, m % 2
+    """Product m of the P V phase: block b = m // (2 NDB) (kb = b // 2,
+    cc = b % 2), db = (m // 2) % NDB, rb = m % 2."""
+    b, db, rb = m // (2 * NDB), (m // 2) % NDB, m % 2
     kb, cc = b // 2, b % 2
     o = m // 2
     slot = VR_BASE + 4 * (o % VRING)
-    dst = O_BASE + 64 * rb + 16 * db
+    dst = O_BASE + 16 * NDB * rb + 16 * db
     p = p_reg(pbuf, rb, kb, cc)
     return Ins(f"v_mfma_f32_32x32x16_bf16 {ar(dst, 16)}, {ar(slot, 4)}, {vr(p, 4)}, {ar(dst, 16)}",
                "mfma", regs_a(dst, 16), regs_a(slot, 4) + regs_v(p, 4), regs_a(dst, 16))
@@ -511,7 +544,7 @@ def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, ta
 
 
 def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring, raw_sched=None):
-    """Scores of the next tile (32 products) beside the second half of the
+    """Scores of the next tile (4 NC products) beside the second half of the
     current tile's weights, then the sum test.  Returns the tile-sum regs."""
     soft = softmax_half(cur, pcur, 1, False, tmp_ring)
     chk, tsums = check_ops()
@@ -519,31 +552,31 @@ def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring, raw_sched=None):
         for ins in soft + chk:
             st.emit(ins)
         return tsums
-    mf = [s_mfma(m, nxt) for m in range(32)]
+    mf = [s_mfma(m, nxt) for m in range(4 * NC)]
     before = [(("K", o), k_read(o, kstage)) for o in range(KAHEAD)]
     sched, need = {}, {}
-    for m in range(32):   # one wait per two operands
+    for m in range(4 * NC):   # one wait per two operands
         o = m // 2
         need[m] = {("K", o), ("K", o + 1)} if o % 2 == 0 else {("K", o)}
-    for o in range(KAHEAD, 16):   # operand o's read after product 2(o - KAHEAD)
+    for o in range(KAHEAD, 2 * NC):   # operand o's read after product 2(o - KAHEAD)
         sched.setdefault(2 * (o - KAHEAD), []).append((("K", o), k_read(o, kstage)))
     interleave(st, mf, before, soft + chk, lds, sched, need, raw_sched=raw_sched)
     return tsums
 
 
 def phase_b(st, lds, cur_p, vstage, nxt, pnxt, final, tmp_ring, prefetched, nextmask=False):
-    """O += V^T P^T for the current tile (32 products) beside the first half
-    of the next tile's weights (its mask first, when it needs one)."""
-    mf = [pv_mfma(m, cur_p) for m in range(32)]
+    """O += V^T P^T for the current tile (8 NDB products) beside the first
+    half of the next tile's weights (its mask first, when it needs one)."""
+    mf = [pv_mfma(m, cur_p) for m in range(8 * NDB)]
     soft = [] if final else softmax_half(nxt, pnxt, 0, True, tmp_ring)
     if nextmask and not final:
         soft = mask_ops(nxt, (0,)) + soft + mask_ops(nxt, (1,)) + thr_step()
     sched, need = {}, {}
-    for m in range(32):   # one wait per two operands
+    for m in range(8 * NDB):   # one wait per two operands
         o = m // 2
         need[m] = ({("V", o, 0), ("V", o, 1), ("V", o + 1, 0), ("V", o + 1, 1)}
                    if o % 2 == 0 else {("V", o, 0), ("V", o, 1)})
-    for o in range(VAHEAD, 16):
+    for o in range(VAHEAD, 4 * NDB):
         reads = v_reads(o, vstage)
         sched.setdefault(2 * (o - VAHEAD) + 1, []).extend([(("V", o, h), reads[h])
                                                            for h in range(2)])
@@ -594,16 +627,17 @@ def slow_path(st, cur, pcur, tmp_ring, back_label):
     # rescale O (AGPRs) 8 registers at a time
     work = [TMP + 8 + i for i in range(8)]
     for rb in range(2):
-        for base in range(0, 64, 8):
+        orb = O_BASE + 16 * NDB * rb
+        for base in range(0, 16 * NDB, 8):
             for i in range(8):
-                st.emit(Ins(f"v_accvgpr_read_b32 {v(work[i])}, {a(O_BASE + 64 * rb + base + i)}",
-                            "valu", [v(work[i])], [a(O_BASE + 64 * rb + base + i)]))
+                st.emit(Ins(f"v_accvgpr_read_b32 {v(work[i])}, {a(orb + base + i)}",
+                            "valu", [v(work[i])], [a(orb + base + i)]))
             for i in range(8):
                 st.emit(Ins(f"v_mul_f32 {v(work[i])}, {v(alpha[rb])}, {v(work[i])}", "valu",
                             [v(work[i])], [v(alpha[rb]), v(work[i])]))
             for i in range(8):
-                st.emit(Ins(f"v_accvgpr_write_b32 {a(O_BASE + 64 * rb + base + i)}, {v(work[i])}",
-                            "accw", [a(O_BASE + 64 * rb + base + i)], [v(work[i])]))
+                st.emit(Ins(f"v_accvgpr_write_b32 {a(orb + base + i)}, {v(work[i])}",
+                            "accw", [a(orb + base + i)], [v(work[i])]))
     ring = tmp_cycle_from(TMP + 16, NTMP - 16 - 4)   # four: one group at a time, unskewed
     for ins in (softmax_half(cur, pcur, 0, True, ring, skew=False)
                 + softmax_half(cur, pcur, 1, False, ring, skew=False)):
@@ -641,9 +675,13 @@ def iteration(out, name, cur, nxt, kstage_read, vstage, kstage_load, vstage_load
         kpre, kloads, kpost = full_loads("K", kstage_load)
         vpre, vloads, vpost = full_loads("V", vstage_load)
         step = [f"s_add_u32 s{S_J}, s{S_J}, 1", f"s_cmp_lt_u32 s{S_J}, s{S_FAST}"]
-        raw_sched = {0: kpre, 1: kloads[:1], 2: kloads[1:2], 3: kloads[2:3],
-                     4: kloads[3:] + kpost + vpre, 5: vloads[:1], 6: vloads[1:2],
-                     7: vloads[2:3], 8: vloads[3:] + vpost + step}
+        # one load after each of the first products: M0 before product 0,
+        # the K loads after products 1 .. NLOAD, then the V loads
+        raw_sched = {0: kpre}
+        for i, l in enumerate(kloads + vloads):
+            raw_sched.setdefault(i + 1, []).append(l)
+        raw_sched[NLOAD] += kpost + vpre
+        raw_sched[2 * NLOAD] += vpost + step
     elif kind in ("gen", "masked"):
         load_block(st, "K", kstage_load, name, can_skip=True, can_tail=True)
         load_block(st, "V", vstage_load, name, can_skip=False, can_tail=kind == "masked")
@@ -675,16 +713,16 @@ def entry(out):
     st = Stream(out)
     st.raw("s_nop 4")
     lds = LdsCounter()
-    mf = [s_mfma(m, 0) for m in range(32)]
+    mf = [s_mfma(m, 0) for m in range(4 * NC)]
     before = [(("K", o), k_read(o, 0)) for o in range(KAHEAD)]
     sched, need = {}, {}
-    for m in range(32):
+    for m in range(4 * NC):
         o = m // 2
         need[m] = {("K", o), ("K", o + 1)} if o % 2 == 0 else {("K", o)}
-    for o in range(KAHEAD, 16):
+    for o in range(KAHEAD, 2 * NC):
         sched.setdefault(2 * (o - KAHEAD), []).append((("K", o), k_read(o, 0)))
     zero = [Ins(f"v_accvgpr_write_b32 {a(O_BASE + i)}, 0", "accw", [a(O_BASE + i)])
-            for i in range(128)]
+            for i in range(32 * NDB)]
     interleave(st, mf, before, zero, lds, sched, need)
     # every wave has read K_0 before iteration 0 loads K_2 into its stage
     st.raw("s_waitcnt lgkmcnt(0)")
@@ -790,21 +828,28 @@ def render(lines):
     clob = ", ".join(f'"{r}"' for r in clobbers())
     return (
         "// Generated by gen_fwd128.py -- do not edit.  The main loop of\n"
-        "// fwd128_kernel (fa_fwd128.hip): see the generator for the schedule.\n"
-        "#define FA_FWD128_LOOP_ASM \\\n" + body.replace("\n", " \\\n") + "\n\n"
-        "#define FA_FWD128_LOOP_CLOBBERS " + clob + "\n"
+        f"// {KERNEL}: see the generator for the schedule.\n"
+        f"#define {MACRO}_ASM \\\n" + body.replace("\n", " \\\n") + "\n\n"
+        f"#define {MACRO}_CLOBBERS " + clob + "\n"
         f"// {len(lines)} lines\n")
 
 
 def main():
-    lines = generate()
-    text = render(lines)
-    if len(sys.argv) > 1 and sys.argv[1] == "--check":
-        cur = open(OUT).read() if os.path.exists(OUT) else ""
-        sys.exit(0 if cur == text else 1)
-    with open(OUT, "w") as f:
-        f.write(text)
-    print(f"wrote {OUT}: {len(lines)} lines")
+    stale = False
+    for d in (128, 64):
+        configure(d)
+        lines = generate()
+        text = render(lines)
+        if len(sys.argv) > 1 and sys.argv[1] == "--check":
+            cur = open(OUT).read() if os.path.exists(OUT) else ""
+            stale |= cur != text
+            continue
+        with open(OUT, "w") as f:
+            f.write(text)
+        print(f"wrote {OUT}: {len(lines)} lines")
+    configure(128)
+    if stale:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -1,10 +1,11 @@
-"""CPU emulation of the generated key loop of the d = 128 forward kernel.
+"""CPU emulation of the generated key loops of the d = 128 and d = 64
+forward kernels.
 
-The instruction text that gen_fwd128.py emits (fa_fwd128_loop.inc) is
-executed for the four waves of one workgroup by the emulator in _emu.py
-(registers, LDS, bounds-checked K/V buffers, barriers).  The setup (registers
-and the three tiles staged before the loop) restates the C++ of
-fa_fwd128.hip.  The output is normalised as the kernel's epilogue does and
+The instruction text that gen_fwd128.py emits (fa_fwd128_loop.inc,
+fa_fwd64_loop.inc) is executed for the four waves of one workgroup by the
+emulator in _emu.py (registers, LDS, bounds-checked K/V buffers, barriers).
+The setup (registers and the three tiles staged before the loop) restates
+the C++ of fa_fwd128.hip / fa_fwd64.hip.  The output is normalised as the kernel's epilogue does and
 compared with the fp64 oracle at the bf16 tolerances.  Hazards and timing
 are not modelled (test_fwd128_schedule.py checks those on the text).
 """
@@ -17,23 +18,39 @@ import torch
 
 import oracle
 from exact_io_aware_45_amd import inputs
-from _emu import Machine, Memory, Program, bf16_bits, bf16_to_f32, tile_swz
+from _emu import Machine, Memory, Program, bf16_bits, bf16_to_f32
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEN = os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", "gen_fwd128.py")
-spec = importlib.util.spec_from_file_location("gen_fwd128_emu", GEN)
-G = importlib.util.module_from_spec(spec)
-spec.loader.exec_module(G)
-LINES = G.generate()
-D, BC, BR = 128, 64, 256
+BC, BR = 64, 256
 
 
-PROGRAM = Program(LINES, ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"), "FA_SLOW")
+def load_gen(d):
+    spec = importlib.util.spec_from_file_location(f"gen_fwd_emu{d}", GEN)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod.configure(d)
+    return mod
 
 
-def emulate_workgroup(q, k, v, N, q0, causal, scale):
+GENS = {d: load_gen(d) for d in (128, 64)}
+PROGRAMS = {d: Program(G.generate(), ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"), "FA_SLOW")
+            for d, G in GENS.items()}
+
+
+def swz_of(D):
+    """The kernels' chunk swizzle of an LDS tile row (tile_swz in fa_common.hpp)."""
+    if D == 128:
+        return lambda r: 4 * (r & 3) + ((r >> 2) & 3)
+    return lambda r: 4 * ((r >> 1) & 1) + ((r >> 2) & 3)
+
+
+def emulate_workgroup(q, k, v, N, q0, causal, scale, D=128):
     """Run the generated loop for the workgroup whose rows start at q0 (one
-    head); returns O [256, 128] (float64, rows past N left 0) and LSE."""
+    head); returns O [256, D] (float64, rows past N left 0) and LSE."""
+    G, PROGRAM, tile_swz = GENS[D], PROGRAMS[D], swz_of(D)
+    NC, NDB, NLOAD = D // 16, D // 32, D // 32
+    LPR = D // 8             # lanes (16-byte chunks) per tile row in a direct load
     KBASE, VBASE = 0x10000000, 0x20000000
     kb = bf16_bits(k).astype(np.uint16).reshape(-1).view(np.uint8).copy()
     vb = bf16_bits(v).astype(np.uint16).reshape(-1).view(np.uint8).copy()
@@ -53,16 +70,13 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
     sl2 = np.float32(scale * 1.4426950408889634)
     qbits = bf16_bits(q)
 
-    def load_tile(buf, t, stage_byte):        # the C++ prologue's load_tile, all waves
-        for w in range(4):
-            for i in range(4):
-                for lane in range(64):
-                    p = (4 * i + w) * 64 + lane
-                    row = p >> 4
-                    qq = (p & 15) ^ tile_swz(row)
-                    src = (min(t * BC + row, N - 1) * D + 8 * qq) * 2
-                    dst = stage_byte + ((4 * i + w) * 64 + lane) * 16
-                    lds[dst:dst + 16] = buf[src:src + 16]
+    def load_tile(buf, t, stage_byte):        # the C++ prologue's tile loads, all waves
+        for row in range(BC):
+            for slot in range(LPR):
+                qq = slot ^ tile_swz(row)
+                src = (min(t * BC + row, N - 1) * D + 8 * qq) * 2
+                dst = stage_byte + row * 2 * D + 16 * slot
+                lds[dst:dst + 16] = buf[src:src + 16]
 
     load_tile(kb, 0, 2 * TILE * 2)
     load_tile(vb, 0, 0)
@@ -76,12 +90,12 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
             h, l32 = lane >> 5, lane & 31
             for rb in range(2):
                 r = min(wrow0 + 32 * rb + l32, N - 1)
-                for c in range(8):
+                for c in range(NC):
                     e = qbits[r, 16 * c + 8 * h:16 * c + 8 * h + 8]
                     for t in range(4):
-                        m.a[G.Q_BASE + 32 * rb + 4 * c + t, lane] = e[2 * t] | (e[2 * t + 1] << 16)
+                        m.a[G.Q_BASE + 4 * NC * rb + 4 * c + t, lane] = e[2 * t] | (e[2 * t + 1] << 16)
             sw_row = tile_swz(l32)
-            for c in range(8):
+            for c in range(NC):
                 m.v[G.KADDR + c, lane] = 2 * (2 * TILE + l32 * D + 8 * ((2 * c + h) ^ sw_row))
             tr_row = 4 * h + ((lane & 15) >> 2)
             tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3)
@@ -90,13 +104,12 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
 
             def tr_off(row, sw, b):
                 return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te
-            for db in range(4):
+            for db in range(NDB):
                 m.v[G.VADDR + 2 * db, lane] = 2 * tr_off(tr_row, sw_lo, db)
                 m.v[G.VADDR + 2 * db + 1, lane] = 2 * tr_off(tr_row + 8, sw_hi, db)
-            for i in range(4):
-                p = (4 * w + i) * 64 + lane
-                row = p >> 4
-                col = 8 * ((p & 15) ^ tile_swz(row))
+            for i in range(NLOAD):
+                row = 16 * w + (BC // 4 // NLOAD) * i + lane // LPR
+                col = 8 * ((lane % LPR) ^ tile_swz(row))
                 m.v[G.GOFF + i, lane] = (row * D + col) * 2 - 1024 * i
                 m.v[G.GOFF_TAIL + i, lane] = ((min(tlast * BC + row, N - 1) - tlast * BC) * D
                                               + col) * 2
@@ -109,8 +122,8 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
         kp, vp = KBASE + 2 * TILE * 2, VBASE + TILE * 2
         m.s[G.S_KPTR], m.s[G.S_KPTR + 1] = kp & 0xFFFFFFFF, kp >> 32
         m.s[G.S_VPTR], m.s[G.S_VPTR + 1] = vp & 0xFFFFFFFF, vp >> 32
-        m.s[G.S_M0K] = 2 * TILE * 2 + w * 4096
-        m.s[G.S_M0V] = w * 4096
+        m.s[G.S_M0K] = 2 * TILE * 2 + w * 32 * D
+        m.s[G.S_M0V] = w * 32 * D
         m.s[G.S_C] = int(np.float32(sl2).view(np.uint32))
         tail = ragged and tend == nt
         m.s[G.S_LAST] = tend - 1
@@ -133,8 +146,8 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale):
                 row = 64 * w + 32 * rb + l32
                 ltot = float(lsum[rb, lane]) + float(lsum[rb, lane ^ 32])
                 L[row] = (float(mref[rb, lane]) + np.log2(ltot)) * np.log(2.0)
-                acc = m.a[G.O_BASE + 64 * rb:G.O_BASE + 64 * rb + 64, lane].view(np.float32)
-                for db in range(4):
+                acc = m.a[G.O_BASE + 16 * NDB * rb:G.O_BASE + 16 * NDB * (rb + 1), lane].view(np.float32)
+                for db in range(NDB):
                     for r in range(16):
                         d = 32 * db + 8 * (r // 4) + 4 * h + r % 4
                         O[row, d] = acc[16 * db + r] / ltot
@@ -183,17 +196,19 @@ def expected_bodies(N, q0, causal):
     return out + ["FIN"]
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("N,q0,causal,kscale", CASES)
-def test_generated_loop_matches_the_oracle(N, q0, causal, kscale):
+def test_generated_loop_matches_the_oracle(N, q0, causal, kscale, D):
     q, k, v = (t[0, 0].float().numpy() for t in inputs.qkv(1, 1, N, D, torch.bfloat16,
                                                              seed=N + q0 + int(causal)))
+    PROGRAM = PROGRAMS[D]
     if kscale != 1.0:
         k[192:] *= kscale
         k = bf16_to_f32(bf16_bits(k))
     scale = D ** -0.5
     PROGRAM.slow_taken = 0
     PROGRAM.bodies_run.clear()
-    O, L = emulate_workgroup(q, k, v, N, q0, causal, scale)
+    O, L = emulate_workgroup(q, k, v, N, q0, causal, scale, D)
     assert [b[3:] for b in PROGRAM.bodies_run] == expected_bodies(N, q0, causal), PROGRAM.bodies_run
     # keys scaled by 3 from key 192 on lift those tiles' weights far past 2^8
     # above the reference set by tile 0: the exact slow path must run there

@@ -1,5 +1,6 @@
-"""Host-side model of the generated main loop of the d = 128 forward kernel
-(exact_io_aware_45_amd/csrc/gen_fwd128.py -> fa_fwd128_loop.inc), CPU only.
+"""Host-side model of the generated main loops of the d = 128 and d = 64
+forward kernels (exact_io_aware_45_amd/csrc/gen_fwd128.py -> fa_fwd128_loop.inc,
+fa_fwd64_loop.inc), CPU only.
 
 The emitted instruction text is parsed and executed on a model of one
 workgroup's LDS and registers:
@@ -29,27 +30,93 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEN = os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", "gen_fwd128.py")
+DIMS = [128, 64]
 
 
-def load_gen():
-    spec = importlib.util.spec_from_file_location("gen_fwd128", GEN)
+def load_gen(d):
+    spec = importlib.util.spec_from_file_location(f"gen_fwd_sched{d}", GEN)
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
+    mod.configure(d)
     return mod
 
 
-G = load_gen()
-LINES = G.generate()
-D = 128
+def swz_of(D):
+    """Chunk swizzle of an LDS tile row (tile_swz in fa_common.hpp)."""
+    if D == 128:
+        return lambda r: 4 * (r & 3) + ((r >> 2) & 3)
+    return lambda r: 4 * ((r >> 1) & 1) + ((r >> 2) & 3)
 
 
-def tile_swz(r):
-    return 4 * (r & 3) + ((r >> 2) & 3)
+class Loop:
+    """One head dim's generated statement and the kernel's per-lane values."""
+
+    def __init__(self, d):
+        self.D = d
+        self.G = load_gen(d)
+        self.LINES = self.G.generate()
+        self.NC, self.NDB, self.NLOAD = d // 16, d // 32, d // 32
+        self.LPR = d // 8                 # 16-byte chunks per tile row
+        self.RPL = 64 // self.LPR         # tile rows per direct load
+        self.STAGE = 64 * d * 2           # bytes of one K or V stage
+        self.WAVE = 32 * d                # bytes of one wave's 16 rows of a tile
+        self.M0K = 2 * self.STAGE         # LDS byte address of K stage 0 (+ wave * WAVE in s64)
+        self.M0V = 0
+        self.swz = swz_of(d)
+        self.KADDR, self.VADDR, self.GOFF = self.kernel_offsets()
+
+    def kernel_offsets(self):
+        """Per-lane values the kernel computes before the loop (restated from
+        fa_fwd128.hip / fa_fwd64.hip): K read addresses (stage 0), V^T read
+        addresses (stage 0), direct-load offsets, in bytes relative to the
+        start of LDS / of a tile."""
+        D, tile_swz = self.D, self.swz
+        kaddr = np.zeros((self.NC, 64), np.int64)
+        vaddr = np.zeros((2 * self.NDB, 64), np.int64)
+        TILE = 64 * D
+        for lane in range(64):
+            h, l32 = lane >> 5, lane & 31
+            sw_row = tile_swz(l32)
+            for c in range(self.NC):
+                kaddr[c, lane] = 2 * (2 * TILE + l32 * D + 8 * ((2 * c + h) ^ sw_row))
+            tr_row = 4 * h + ((lane & 15) >> 2)
+            tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3)
+            sw_lo, sw_hi = tile_swz(tr_row), tile_swz(tr_row + 8)
+            tq, te = tr_col >> 3, tr_col & 7
+
+            def tr_off(row, sw, b):
+                return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te
+            for db in range(self.NDB):
+                vaddr[2 * db, lane] = 2 * tr_off(tr_row, sw_lo, db)
+                vaddr[2 * db + 1, lane] = 2 * tr_off(tr_row + 8, sw_hi, db)
+        goff = np.zeros((4, self.NLOAD, 64), np.int64)   # [wave][load][lane]
+        for w in range(4):
+            for i in range(self.NLOAD):
+                for lane in range(64):
+                    row = 16 * w + self.RPL * i + lane // self.LPR
+                    col = 8 * ((lane % self.LPR) ^ tile_swz(row))
+                    goff[w, i, lane] = 2 * (row * D + col) - 1024 * i
+        return kaddr, vaddr, goff
+
+    def section(self, start_label, end_marker):
+        """Lines from a label up to (excluding) the first line starting with end_marker."""
+        i = self.LINES.index(start_label)
+        out = []
+        for l in self.LINES[i + 1:]:
+            if l.startswith(end_marker):
+                break
+            out.append(l)
+        return out
 
 
-def test_committed_loop_matches_the_generator():
-    text = G.render(LINES)
-    assert open(G.OUT).read() == text, "fa_fwd128_loop.inc is stale: rerun gen_fwd128.py"
+LOOPS = {d: Loop(d) for d in DIMS}
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_committed_loop_matches_the_generator(d):
+    L = LOOPS[d]
+    text = L.G.render(L.LINES)
+    assert open(L.G.OUT).read() == text, f"{L.G.OUT} is stale: rerun gen_fwd128.py"
 
 
 # ------------------------------------------------------------- parsing
@@ -77,53 +144,7 @@ def split(line):
     return op, args
 
 
-def section(start_label, end_marker):
-    """Lines from a label up to (excluding) the first line starting with end_marker."""
-    i = LINES.index(start_label)
-    out = []
-    for l in LINES[i + 1:]:
-        if l.startswith(end_marker):
-            break
-        out.append(l)
-    return out
-
-
 # --------------------------------------------------------- lane-level model
-def kernel_offsets():
-    """Per-lane values the kernel computes before the loop (restated from
-    fa_fwd128.hip): K read addresses (stage 0), V^T read addresses (stage 0),
-    direct-load offsets, all in bytes relative to the start of LDS / of a tile."""
-    kaddr = np.zeros((8, 64), np.int64)
-    vaddr = np.zeros((8, 64), np.int64)
-    TILE = 64 * D
-    for lane in range(64):
-        h, l32 = lane >> 5, lane & 31
-        sw_row = tile_swz(l32)
-        for c in range(8):
-            kaddr[c, lane] = 2 * (2 * TILE + l32 * D + 8 * ((2 * c + h) ^ sw_row))
-        tr_row = 4 * h + ((lane & 15) >> 2)
-        tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3)
-        sw_lo, sw_hi = tile_swz(tr_row), tile_swz(tr_row + 8)
-        tq, te = tr_col >> 3, tr_col & 7
-
-        def tr_off(row, sw, b):
-            return row * D + 8 * (((4 * b) ^ (sw & 12)) | (tq ^ (sw & 3))) + te
-        for db in range(4):
-            vaddr[2 * db, lane] = 2 * tr_off(tr_row, sw_lo, db)
-            vaddr[2 * db + 1, lane] = 2 * tr_off(tr_row + 8, sw_hi, db)
-    goff = np.zeros((4, 4, 64), np.int64)   # [wave][load][lane]
-    for w in range(4):
-        for i in range(4):
-            for lane in range(64):
-                p = (4 * w + i) * 64 + lane
-                row = p >> 4
-                goff[w, i, lane] = 2 * (row * D + 8 * ((p & 15) ^ tile_swz(row))) - 1024 * i
-    return kaddr, vaddr, goff
-
-
-KADDR, VADDR, GOFF = kernel_offsets()
-M0K = 32768   # LDS byte address of K stage 0 (+ wave * 4096 in s64)
-M0V = 0
 NONE = 0xFFFFFFFF
 
 
@@ -159,25 +180,29 @@ def follow(lines, env):
     return out
 
 
-# scalar registers of one step for each load case: tile j = 5; whole loads,
-# the clamped K tile, no K tile, or no K tile and the clamped V tile
-LOAD_CASES = {
-    "whole": {G.S_KEND: 10, G.S_KTAILJ: NONE, G.S_VTAILJ: NONE},
-    "ktail": {G.S_KEND: 10, G.S_KTAILJ: 5, G.S_VTAILJ: NONE},
-    "kskip": {G.S_KEND: 5, G.S_KTAILJ: NONE, G.S_VTAILJ: NONE},
-    "vtail": {G.S_KEND: 5, G.S_KTAILJ: NONE, G.S_VTAILJ: 5},
-}
+# the load cases of one step, tile j = 5: whole loads, the clamped K tile,
+# no K tile, or no K tile and the clamped V tile (SGPR numbers are the same
+# at both head dims)
+def load_cases(G):
+    return {
+        "whole": {G.S_KEND: 10, G.S_KTAILJ: NONE, G.S_VTAILJ: NONE},
+        "ktail": {G.S_KEND: 10, G.S_KTAILJ: 5, G.S_VTAILJ: NONE},
+        "kskip": {G.S_KEND: 5, G.S_KTAILJ: NONE, G.S_VTAILJ: NONE},
+        "vtail": {G.S_KEND: 5, G.S_KTAILJ: NONE, G.S_VTAILJ: 5},
+    }
 
 
-def env_of(case):
-    return {**LOAD_CASES[case], G.S_J: 5, G.S_FAST: 0}
+def env_of(L, case):
+    G = L.G
+    return {**load_cases(G)[case], G.S_J: 5, G.S_FAST: 0}
 
 
-def stage_tiles(lines, ktile, vtile, tail_offs=None):
+def stage_tiles(L, lines, ktile, vtile, tail_offs=None):
     """Execute the direct loads in `lines` for all four waves into a 64 KiB LDS
     image (uint16 elements): whole-tile loads use the kernel's offsets, the
     clamped ones `tail_offs`; the instruction offset applies to both
     addresses.  Returns the image and {(K|V, stage, clamped)} loaded."""
+    G = L.G
     lds = np.full(32768, -1, np.int64)
     loaded = set()
     for w in range(4):
@@ -185,14 +210,14 @@ def stage_tiles(lines, ktile, vtile, tail_offs=None):
         for l in lines:
             op, args = split(l)
             if op == "s_add_u32" and args[0] == "m0":
-                m0 = {"s64": M0K, "s65": M0V}[args[1]] + 4096 * w + int(args[2])
+                m0 = {"s64": L.M0K, "s65": L.M0V}[args[1]] + L.WAVE * w + int(args[2])
             elif op == "global_load_lds_dwordx4":
                 reg = int(args[0][1:])
                 clamped = reg >= G.GOFF_TAIL
                 i = reg - (G.GOFF_TAIL if clamped else G.GOFF)
-                assert 0 <= i < 4, l
+                assert 0 <= i < L.NLOAD, l
                 off = int(args[2].split(":")[1]) if len(args) > 2 else 0
-                offs = tail_offs if clamped else GOFF
+                offs = tail_offs if clamped else L.GOFF
                 is_k = args[1] == f"s[{G.S_KPTR}:{G.S_KPTR + 1}]"
                 flat = (ktile if is_k else vtile).reshape(-1)
                 for lane in range(64):
@@ -200,8 +225,8 @@ def stage_tiles(lines, ktile, vtile, tail_offs=None):
                     dst = (m0 + off + 16 * lane) // 2
                     assert 0 <= src and src + 8 <= flat.size
                     lds[dst:dst + 8] = flat[src:src + 8]
-                base = M0K if is_k else M0V
-                loaded.add(("K" if is_k else "V", (m0 - base - 4096 * w) // 16384, clamped))
+                base = L.M0K if is_k else L.M0V
+                loaded.add(("K" if is_k else "V", (m0 - base - L.WAVE * w) // L.STAGE, clamped))
     return lds, loaded
 
 
@@ -217,22 +242,20 @@ def tr_read(lds, addrs):
     return out
 
 
-def run_operand_model(body, kstage, vstage):
+def run_operand_model(L, body, kstage, vstage):
     """Follow every LDS operand read of `body` into its product and check the
     operand each lane receives."""
+    G, D = L.G, L.D
     # element values encode (row, col) so every mismatch is visible
     ktile = np.arange(64 * D).reshape(64, D) + 10 ** 6
     vtile = np.arange(64 * D).reshape(64, D) + 2 * 10 ** 6
     lds = np.full(32768, -1, np.int64)
-    kb0 = 2 * 64 * D
-    for stage in range(2):
-        lds[kb0 + stage * 8192: kb0 + stage * 8192 + 8192] = -1
     # place the tiles the way the direct loads do (checked separately)
     for r in range(64):
-        for q in range(16):
-            slot = q ^ tile_swz(r)
-            kdst = (M0K + kstage * 16384) // 2 + r * D + 8 * slot
-            vdst = (M0V + vstage * 16384) // 2 + r * D + 8 * slot
+        for q in range(L.LPR):
+            slot = q ^ L.swz(r)
+            kdst = (L.M0K + kstage * L.STAGE) // 2 + r * D + 8 * slot
+            vdst = (L.M0V + vstage * L.STAGE) // 2 + r * D + 8 * slot
             lds[kdst:kdst + 8] = ktile[r, 8 * q:8 * q + 8]
             lds[vdst:vdst + 8] = vtile[r, 8 * q:8 * q + 8]
     ring = {}   # agpr -> per-lane values (one column per register half)
@@ -242,19 +265,21 @@ def run_operand_model(body, kstage, vstage):
         if op == "ds_read_b128":
             dst = regs(args[0])
             c = int(args[1][1:]) - G.KADDR
+            assert 0 <= c < L.NC, l
             off = int(args[2].split(":")[1]) if len(args) > 2 else 0
-            assert (off // 16384) == kstage
+            assert (off // L.STAGE) == kstage
             vals = np.zeros((64, 8), np.int64)
             for lane in range(64):
-                a0 = (KADDR[c, lane] + off) // 2
+                a0 = (L.KADDR[c, lane] + off) // 2
                 vals[lane] = lds[a0:a0 + 8]
             ring[dst[0]] = ("K", vals)
         elif op == "ds_read_b64_tr_b16":
             dst = regs(args[0])
             idx = int(args[1][1:]) - G.VADDR
+            assert 0 <= idx < 2 * L.NDB, l
             off = int(args[2].split(":")[1]) if len(args) > 2 else 0
-            assert (off // 16384) == vstage
-            vals = tr_read(lds, VADDR[idx] + off)
+            assert (off // L.STAGE) == vstage
+            vals = tr_read(lds, L.VADDR[idx] + off)
             ring[dst[0]] = ("V", vals)
         elif op == "v_mfma_f32_32x32x16_bf16":
             dst, sa, sb = regs(args[0]), regs(args[1]), regs(args[2])
@@ -265,7 +290,8 @@ def run_operand_model(body, kstage, vstage):
                 assert lo[0] == "V" and hi[0] == "V"
                 A = np.concatenate([lo[1], hi[1]], axis=1)   # lane x 8 (k = 8h + t)
                 o = int(dst[0][1:]) - G.O_BASE
-                rb, db = o // 64, (o % 64) // 16
+                rb, db = o // (16 * L.NDB), (o % (16 * L.NDB)) // 16
+                assert rb < 2
                 p = int(sb[0][1:])
                 pb = 0 if p < G.P_BASE[1] else 1
                 rel = p - G.P_BASE[pb]
@@ -282,7 +308,8 @@ def run_operand_model(body, kstage, vstage):
                 kv = ring[sa[0]]
                 assert kv[0] == "K"
                 q = int(sb[0][1:]) - G.Q_BASE
-                rb, c = q // 32, (q % 32) // 4
+                rb, c = q // (4 * L.NC), (q % (4 * L.NC)) // 4
+                assert rb < 2
                 s = int(dst[0][1:])
                 buf = 0 if s < G.S_BASE[1] else 1
                 rel = s - G.S_BASE[buf]
@@ -306,56 +333,64 @@ BODIES = {  # name: (label, K read stage, V read stage, K load stage, V load sta
 }
 # the load cases each body can meet: the straight body only whole tiles, the
 # general unmasked one never the clamped V tile (tile j + 1 would be masked)
+ALL_CASES = ["whole", "ktail", "kskip", "vtail"]
 BODY_CASES = {"A": ["whole"], "B": ["whole"], "GA": ["whole", "ktail", "kskip"],
-              "GB": ["whole", "ktail", "kskip"], "MA": list(LOAD_CASES), "MB": list(LOAD_CASES),
+              "GB": ["whole", "ktail", "kskip"], "MA": ALL_CASES, "MB": ALL_CASES,
               "FA": ["whole"], "FB": ["whole"]}
 
 
-def body_of(name):
-    return section(BODIES[name][0], "s_barrier")
+def body_of(L, name):
+    return L.section(BODIES[name][0], "s_barrier")
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("name", list(BODIES))
-def test_operands_of_every_product(name):
+def test_operands_of_every_product(name, d):
+    L = LOOPS[d]
     _, kst, vst, _, _, final = BODIES[name]
-    checked = run_operand_model(body_of(name), kst, vst)
-    assert checked == ({"k": 0, "v": 32} if final else {"k": 32, "v": 32})
+    checked = run_operand_model(L, body_of(L, name), kst, vst)
+    nk, nv = 4 * L.NC, 8 * L.NDB
+    assert checked == ({"k": 0, "v": nv} if final else {"k": nk, "v": nv})
 
 
-def test_operands_of_the_first_tile_scores():
+@pytest.mark.parametrize("d", DIMS)
+def test_operands_of_the_first_tile_scores(d):
     """The entry computes tile 0's scores from K stage 0."""
-    body = LINES[:LINES.index("s_cbranch_scc1 FA_EMASK_%=")]
-    checked = run_operand_model(body, 0, 0)
-    assert checked == {"k": 32, "v": 0}
+    L = LOOPS[d]
+    body = L.LINES[:L.LINES.index("s_cbranch_scc1 FA_EMASK_%=")]
+    checked = run_operand_model(L, body, 0, 0)
+    assert checked == {"k": 4 * L.NC, "v": 0}
 
 
-def tail_offsets(N, tlast):
+def tail_offsets(L, N, tlast):
     """Clamped direct-load offsets of the partial last tile (the kernel's
     formula): rows past N - 1 repeat row N - 1."""
-    out = np.zeros((4, 4, 64), np.int64)
+    out = np.zeros((4, L.NLOAD, 64), np.int64)
     for w in range(4):
-        for i in range(4):
+        for i in range(L.NLOAD):
             for lane in range(64):
-                p = (4 * w + i) * 64 + lane
-                row = p >> 4
-                col = 8 * ((p & 15) ^ tile_swz(row))
-                out[w, i, lane] = 2 * ((min(tlast * 64 + row, N - 1) - tlast * 64) * D + col)
+                row = 16 * w + L.RPL * i + lane // L.LPR
+                col = 8 * ((lane % L.LPR) ^ L.swz(row))
+                out[w, i, lane] = 2 * ((min(tlast * 64 + row, N - 1) - tlast * 64) * L.D + col)
     return out
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("name,case", [(n, c) for n in BODIES for c in BODY_CASES[n]])
-def test_direct_loads_place_tiles_as_the_reads_expect(name, case):
+def test_direct_loads_place_tiles_as_the_reads_expect(name, case, d):
     """The emitted loads (M0 values, offset registers, instruction offsets)
     write chunk q of tile row r to slot q ^ swz(r) of the right stage, for
     all four waves, and cover each loaded stage exactly once; a partial last
     tile (here 37 rows) goes through the clamped offsets, its missing rows
     repeating the last one; a tile past the end is not loaded."""
+    L = LOOPS[d]
+    D = L.D
     _, _, _, kst, vst, final = BODIES[name]
     N, tlast = 3 * 64 + 37, 3
     ktile = np.arange(64 * D).reshape(64, D) + 10 ** 6
     vtile = np.arange(64 * D).reshape(64, D) + 2 * 10 ** 6
-    lines = follow(body_of(name), env_of(case))
-    lds, loaded = stage_tiles(lines, ktile, vtile, tail_offsets(N, tlast))
+    lines = follow(body_of(L, name), env_of(L, case))
+    lds, loaded = stage_tiles(L, lines, ktile, vtile, tail_offsets(L, N, tlast))
     want = set() if final else {
         "whole": {("K", kst, False), ("V", vst, False)},
         "ktail": {("K", kst, True), ("V", vst, False)},
@@ -363,18 +398,19 @@ def test_direct_loads_place_tiles_as_the_reads_expect(name, case):
         "vtail": {("V", vst, True)}}[case]
     assert loaded == want
     for which, stage, clamped in loaded:
-        tile, base = (ktile, M0K) if which == "K" else (vtile, M0V)
+        tile, base = (ktile, L.M0K) if which == "K" else (vtile, L.M0V)
         for r in range(64):
             src = min(r, 36) if clamped else r
-            for q in range(16):
-                at = (base + stage * 16384) // 2 + r * D + 8 * (q ^ tile_swz(r))
+            for q in range(L.LPR):
+                at = (base + stage * L.STAGE) // 2 + r * D + 8 * (q ^ L.swz(r))
                 assert np.array_equal(lds[at:at + 8], tile[src, 8 * q:8 * q + 8])
     assert (lds >= 0).sum() == len(loaded) * 64 * D
 
 
-def mask_semantics(lines):
+def mask_semantics(L, lines):
     """(score register, constant) pairs of the emitted mask: the compare
     `v_cmp_gt_i32 s[p], OFF, THR[rb]` feeds the next cndmask on s[p]."""
+    G = L.G
     pend, out = {}, []
     for l in lines:
         op, args = split(l)
@@ -387,21 +423,23 @@ def mask_semantics(lines):
     return out
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("where", ["entry", "MA", "MB"])
-def test_masks_hide_exactly_the_invisible_keys(where):
+def test_masks_hide_exactly_the_invisible_keys(where, d):
     """For every lane, row and tile position, the emitted compares mask a
     score iff its key is past the row's last visible key (key > row when
     causal, key >= N always), with the kernel's threshold formula."""
+    L = LOOPS[d]
     if where == "entry":
-        lines = section("s_cbranch_scc1 FA_EMASK_%=", "FA_EMASK_%=:")
+        lines = L.section("s_cbranch_scc1 FA_EMASK_%=", "FA_EMASK_%=:")
         buf = 0
     else:
-        lines = body_of(where)
+        lines = body_of(L, where)
         buf = 1 if where == "MA" else 0
-    sem = mask_semantics(lines)
+    sem = mask_semantics(L, lines)
     assert len(sem) == 64
     regs_seen = sorted(r for r, _, _ in sem)
-    base = G.S_BASE[buf]
+    base = L.G.S_BASE[buf]
     assert regs_seen == list(range(base, base + 64))
     for (N, causal, t, wrow0) in ((1000, True, 12, 768), (1000, False, 15, 512), (700, True, 10, 640),
                                   (130, False, 2, 0), (300, True, 4, 256)):
@@ -442,31 +480,35 @@ def classify(op):
     return "other"
 
 
-def straight_paths():
+def straight_paths(L):
     """Instruction sequences as executed: the entry (with and without the
     first tile's mask), each loop body for each load case it can meet, on
     its fast path and with its slow path spliced in at its branch."""
+    LINES = L.LINES
     paths = []
     entry = LINES[:LINES.index("FA_LA_%=:")]
     i, j = entry.index("s_cbranch_scc1 FA_EMASK_%="), entry.index("FA_EMASK_%=:")
     paths += [entry, entry[:i] + entry[j:]]
     for name in BODIES:
         for case in BODY_CASES[name]:
-            body = follow(body_of(name), env_of(case))
+            body = follow(body_of(L, name), env_of(L, case))
             paths.append(body)
-            slow = section(f"FA_SLOW{name}_%=:", "s_branch")
+            slow = L.section(f"FA_SLOW{name}_%=:", "s_branch")
             i = body.index(f"s_cbranch_vccnz FA_SLOW{name}_%=")
             j = body.index(f"FA_PB{name}_%=:")
             paths.append(body[:i] + slow + body[j:])
     return paths
 
 
-NPATHS = len(straight_paths())
+PATHS = {d: straight_paths(L) for d, L in LOOPS.items()}
+NPATHS = len(PATHS[128])
+assert all(len(p) == NPATHS for p in PATHS.values())
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("path", range(NPATHS))
-def test_lds_operands_landed_and_rings_not_overwritten_in_flight(path):
-    body = straight_paths()[path]
+def test_lds_operands_landed_and_rings_not_overwritten_in_flight(path, d):
+    body = PATHS[d][path]
     pending = []          # outstanding LDS reads: list of register sets
     last_use = {}         # agpr -> index of the last product reading it
     n_mfma = 0
@@ -485,6 +527,7 @@ def test_lds_operands_landed_and_rings_not_overwritten_in_flight(path):
                 if r in last_use:
                     assert n_mfma - last_use[r] >= 1, (l, r)
             pending.append(dst)
+            assert len(pending) <= 15, "more LDS reads in flight than lgkmcnt counts"
         elif op == "ds_bpermute_b32":
             pending.append(set(regs(args[0])))
         elif op.startswith("v_mfma"):
@@ -502,15 +545,16 @@ def test_lds_operands_landed_and_rings_not_overwritten_in_flight(path):
                 assert not (p & used), ("LDS result read before it landed", l)
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("path", range(NPATHS))
-def test_matrix_vector_hazards(path):
+def test_matrix_vector_hazards(path, d):
     """Wait states (instructions issued; s_nop n counts n + 1) between a
     product writing a register and a vector/LDS instruction reading it >= 12
     (gfx950, 8-pass 32x32x16 product), between a vector write and a product
     reading it >= 2, between an exponential and its reader >= 1, between a
     dot product and any reader of its result (its own accumulation included)
     >= 3, between a vector write and a dot product reading it >= 2."""
-    body = straight_paths()[path]
+    body = PATHS[d][path]
     t = 0
     last = {}   # reg -> (kind, time)
     for l in body:
@@ -557,11 +601,13 @@ def test_matrix_vector_hazards(path):
         t += wait_states(l)
 
 
-def test_every_barrier_waits_for_the_direct_loads():
+@pytest.mark.parametrize("d", DIMS)
+def test_every_barrier_waits_for_the_direct_loads(d):
     """A barrier that follows direct loads is preceded by vmcnt(0); the one
     after the first tile's scores (no loads since the prologue's) waits for
     the wave's LDS reads instead, so no wave reloads K stage 0 while another
     still reads it."""
+    LINES = LOOPS[d].LINES
     loads_since = False
     for i, l in enumerate(LINES):
         if l.startswith("global_load_lds"):
@@ -575,9 +621,10 @@ def test_every_barrier_waits_for_the_direct_loads():
     assert not any(x.startswith("global_load_lds") for x in LINES[:first])
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("path", range(NPATHS))
-def test_m0_set_at_least_one_state_before_each_direct_load(path):
-    body = straight_paths()[path]
+def test_m0_set_at_least_one_state_before_each_direct_load(path, d):
+    body = PATHS[d][path]
     last_m0 = None
     for i, l in enumerate(body):
         if l.startswith("s_add_u32 m0,"):
@@ -586,14 +633,16 @@ def test_m0_set_at_least_one_state_before_each_direct_load(path):
             assert last_m0 is not None and i - last_m0 >= 2, (path, i, l)
 
 
-def test_straight_body_keeps_its_branch_condition():
+@pytest.mark.parametrize("d", DIMS)
+def test_straight_body_keeps_its_branch_condition(d):
     """The straight body compares the next tile index with the straight
     limit early and branches on SCC after its barrier: nothing in between
     (its slow path included) may write SCC."""
+    L = LOOPS[d]
     for P in "AB":
-        body = section(f"FA_BODY{P}_%=:", "s_cbranch_scc1 FA_BODY")
-        k = body.index(f"s_cmp_lt_u32 s{G.S_J}, s{G.S_FAST}")
-        slow = section(f"FA_SLOW{P}_%=:", "s_branch")
+        body = L.section(f"FA_BODY{P}_%=:", "s_cbranch_scc1 FA_BODY")
+        k = body.index(f"s_cmp_lt_u32 s{L.G.S_J}, s{L.G.S_FAST}")
+        slow = L.section(f"FA_SLOW{P}_%=:", "s_branch")
         for l in body[k + 1:] + slow:
             op = l.split()[0]
             assert not op.startswith("s_") or op in (
@@ -601,11 +650,12 @@ def test_straight_body_keeps_its_branch_condition():
 
 
 # ------------------------------------------------------------ tile counts
-def run_control(N, q0, causal):
+def run_control(L, N, q0, causal):
     """Execute the scalar part of the whole statement with the kernel's
     start values (no slow path): which K and V tiles get loaded (and whether
     through the clamped offsets), which tiles get masked, which body each
     step takes."""
+    G, LINES = L.G, L.LINES
     BC, BR = 64, 256
     nt = -(-N // BC)
     qmax = min(q0 + BR, N) - 1
@@ -618,7 +668,7 @@ def run_control(N, q0, causal):
         fm = min(fm, nt - 1)
     tail = ragged and tend == nt
     kfull = nt - 1 if tail else tend
-    TB = 64 * 256
+    TB = 64 * 2 * L.D
     KB, VB = 1 << 40, 2 << 40
     s = {G.S_LAST: tend - 1, G.S_KEND: max(0, tend - 2),
          G.S_KTAILJ: nt - 3 if tail and nt >= 3 else NONE,
@@ -669,17 +719,18 @@ def run_control(N, q0, causal):
     return tend, fm, kload, vload, masked, bodies
 
 
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 200, 256, 300, 511, 512,
                                700, 1000, 1024, 8192])
-def test_loop_loads_and_masks(N, causal):
+def test_loop_loads_and_masks(N, causal, d):
     """Every tile in [0, tend) is loaded once, in order, whole tiles through
     the plain offsets and only a partial last tile through the clamped ones;
     exactly the tiles that hold an invisible key are masked; every step
     before the last takes the straight body when its next tile is unmasked
     and both its loads are whole tiles."""
     for q0 in range(0, N, 256):
-        tend, fm, kload, vload, masked, bodies = run_control(N, q0, causal)
+        tend, fm, kload, vload, masked, bodies = run_control(LOOPS[d], N, q0, causal)
         assert [t for t, _ in kload] == list(range(tend))
         assert [t for t, _ in vload] == list(range(tend))
         for t, clamped in kload[2:] + vload[1:]:

@@ -180,30 +180,33 @@ def test_forward_full_workloads(name, seed):
     forward_parity_all_heads(x["q"], x["k"], x["v"], w.causal)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 50, 64, 65, 128, 129, 192, 200, 333, 600])
-def test_forward_eight_wave_grid(N, causal):
-    """Enough heads (B4 H130) that the launch takes 8-wave workgroups (the
-    long-sequence configuration) at short, ragged N: 1, 2, 3, ... key tiles
-    per workgroup, so the K/V staging ring starts and ends at every phase."""
+def test_forward_resident_grid(N, causal, d):
+    """Enough heads (B4 H130: at least one 256-row query tile per CU) that
+    the launch takes the resident hand-scheduled kernel of its head dim, at
+    short, ragged N: 1, 2, 3, ... key tiles per item, so the K/V stages
+    start and end at every phase."""
     need_gpu()
-    log(f"forward bf16 B4 H130 N{N} d128 causal={causal} (8-wave grid)")
-    q, k, v = inputs.qkv(4, 130, N, 128, torch.bfloat16, seed=1000 + N)
+    log(f"forward bf16 B4 H130 N{N} d{d} causal={causal} (resident grid)")
+    q, k, v = inputs.qkv(4, 130, N, d, torch.bfloat16, seed=1000 + N + d)
     forward_parity_all_heads(q, k, v, causal, chunk=130)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [700, 1500])
-def test_forward_reference_moves_mid_sequence(N, causal):
+def test_forward_reference_moves_mid_sequence(N, causal, d):
     """Keys from the fourth 64-key tile on scaled by 3, so that those tiles'
     scores exceed the running reference set by the first tiles by far more
-    than 2^3 per weight: the hand-scheduled d = 128 loop must take its exact
-    path (row maximum, rescale, recomputed weights) there, in the launch
+    than 2^3 per weight: the hand-scheduled loop must take its exact path
+    (row maximum, rescale, recomputed weights) there, in the launch
     configuration of the long workloads (B2 H130: more than one 256-row
     workgroup per CU)."""
     need_gpu()
-    log(f"forward bf16 B2 H130 N{N} d128 causal={causal}, keys x3 from key 192 on")
-    q, k, v = inputs.qkv(2, 130, N, 128, torch.bfloat16, seed=2000 + N)
+    log(f"forward bf16 B2 H130 N{N} d{d} causal={causal}, keys x3 from key 192 on")
+    q, k, v = inputs.qkv(2, 130, N, d, torch.bfloat16, seed=2000 + N + d)
     kscale = torch.ones(N, dtype=torch.float32)
     kscale[192:] = 3.0
     k = (k.float() * kscale[None, None, :, None]).to(torch.bfloat16)
@@ -353,13 +356,15 @@ def test_backward_resident_grid(N, causal):
     backward_parity_all_heads(q, k, v, do, causal, chunk=65)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_resident_dq_grouped_heads(causal):
-    """Grouped K/V heads (130 query heads over 26) through the resident dQ
-    kernel: each query head reads its group's K and V."""
+def test_backward_resident_dq_grouped_heads(causal, d):
+    """Grouped K/V heads (130 query heads over 26) through the resident
+    forward kernels and the resident dQ kernel (d = 128): each query head
+    reads its group's K and V."""
     need_gpu()
-    log(f"gqa backward B2 H130 Hkv26 N333 d128 causal={causal} (resident dQ)")
-    gqa_parity(2, 130, 26, 333, 128, causal, seed=44)
+    log(f"gqa forward+backward B2 H130 Hkv26 N333 d{d} causal={causal} (resident)")
+    gqa_parity(2, 130, 26, 333, d, causal, seed=44 + d)
 
 
 @pytest.mark.parametrize("causal", [False, True])
