@@ -190,6 +190,10 @@ void fwd128_kernel(FwdArgs a) {
     const uint32_t svtail = uni(tail && nt >= 2 ? (uint32_t)(nt - 2) : ~0u);
     const uint32_t sfm = uni((uint32_t)fm);
     const uint32_t sfast = uni((uint32_t)max(0, min(fm - 1, kfull - 2)));
+    // This wave's last tile holding a key it sees (causal: the tile of its
+    // last row); past it the loop only loads and meets the barriers.
+    const uint32_t swdiag =
+        uni((uint32_t)(CAUSAL ? min(tend - 1, min(wrow0 + 63, N - 1) / BC) : tend - 1));
     const uint32_t bperm = (uint32_t)((lane ^ 32) << 2);
     const float ninf = -INFINITY;
     // This item's first K and V tiles (loaded while the previous output was
@@ -222,7 +226,8 @@ void fwd128_kernel(FwdArgs a) {
                    "{v[192:199]}"(kaddr), "{v[200:207]}"(vaddr), "{v[208:211]}"(goff),
                    "{v224}"(bperm), "{v251}"(ninf), "{v[252:255]}"(gtail),
                    "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s67}"(slast), "{s68}"(skend),
-                   "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast)
+                   "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast),
+                   "{s83}"(swdiag)
                  : FA_FWD128_LOOP_CLOBBERS);
     const float m_ref[2] = {-mneg0, -mneg1};
     const float lsum[2] = {l0, l1};

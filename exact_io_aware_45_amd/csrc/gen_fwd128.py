@@ -41,7 +41,9 @@ How it is laid out is specific to gfx950:
     scores and their exact row maxima (the first reference), every tile
     after it, and the masked ones at the end (causal diagonal tiles, the
     ragged tail), whose scores are set to -inf where key > row or key >= N
-    by one threshold compare per element before their exponentials.
+    by one threshold compare per element before their exponentials.  Causal
+    tiles wholly past a wave's last row hold no visible key for it: from
+    there on the wave only issues its share of the loads and the barriers.
 
 The generator also checks its own output: data hazards between matrix and
 vector instructions (wait states counted in instructions, conservatively),
@@ -105,6 +107,8 @@ S_T = 73          # scratch
 S_MASK = (74, 76, 78, 80)   # SGPR pairs for element masks
 S_FAST = 82       # iterations j < this take the straight body: tile j + 1 needs no
                   # mask and both of its loads are whole tiles
+S_WDIAG = 83      # this wave's last tile holding a visible key (causal: the tile of
+                  # its last row); iterations past it only load and synchronise
 
 # LDS map (bytes): V stage 0 at 0, V stage 1 at STAGE_BYTES, K stage 0 at
 # 2 STAGE_BYTES, K stage 1 at 3 STAGE_BYTES (one 64-key tile each: 16 KiB at
@@ -784,6 +788,8 @@ def generate():
         out.append(f"s_cbranch_scc1 FA_BODY{Q}_%=")
         out.append(f"s_branch FA_GEN{Q}_%=")
         out.append(f"FA_GEN{P}_%=:")
+        out.append(f"s_cmp_gt_u32 s{S_J}, s{S_WDIAG}")
+        out.append(f"s_cbranch_scc1 FA_IDLE{P}_%=")
         out.append(f"s_cmp_eq_u32 s{S_J}, s{S_LAST}")
         out.append(f"s_cbranch_scc1 FA_FIN{P}_%=")
         out.append(f"s_add_u32 s{S_T}, s{S_J}, 1")
@@ -797,6 +803,24 @@ def generate():
         slows.append(iteration(out, "M" + P, *stages(parity), "masked"))
         out.append(f"s_add_u32 s{S_J}, s{S_J}, 1")
         out.append(f"s_branch FA_L{Q}_%=")
+        # idle steps: tile j holds no key this wave sees, nor does any later
+        # one; the wave still loads its rows of K_{j+2} and V_{j+1} and meets
+        # the barrier, and ends with the others at the last tile
+        out.append(f"FA_IDLE{P}_%=:")
+        out.append(f"s_cmp_eq_u32 s{S_J}, s{S_LAST}")
+        out.append("s_cbranch_scc1 FA_IDLEF_%=")
+        st = Stream(out)
+        _, _, _, _, kload, vload = stages(parity)
+        load_block(st, "K", kload, "I" + P, can_skip=True, can_tail=True)
+        load_block(st, "V", vload, "I" + P, can_skip=False, can_tail=True)
+        out.append("s_waitcnt vmcnt(0)")
+        out.append("s_barrier")
+        out.append(f"s_add_u32 s{S_J}, s{S_J}, 1")
+        out.append(f"s_branch FA_IDLE{Q}_%=")
+    out.append("FA_IDLEF_%=:")
+    out.append("s_waitcnt vmcnt(0)")
+    out.append("s_barrier")
+    out.append("s_branch FA_DONE_%=")
     for parity, P in ((0, "A"), (1, "B")):
         out.append(f"FA_FIN{P}_%=:")
         slows.append(iteration(out, "F" + P, *stages(parity), "final"))

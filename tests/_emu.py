@@ -186,8 +186,8 @@ def lane_bf16(m, tok):
 
 class Program:
     """A parsed statement.  body_kinds: label prefixes whose entries wave 0
-    records (in order) in bodies_run; slow_prefix: branch targets counted in
-    slow_taken when taken."""
+    records (in order) in bodies_run, and every wave w in bodies_by_wave[w];
+    slow_prefix: branch targets counted in slow_taken when taken."""
 
     def __init__(self, lines, body_kinds=(), slow_prefix=None):
         self.prog, self.labels = parse(lines)
@@ -199,12 +199,15 @@ class Program:
         self.slow_prefix = slow_prefix
         self.slow_taken = 0
         self.bodies_run = []
+        self.bodies_by_wave = {}
 
     def run_wave(self, m, lds, mem, pc, wave=0):
         """Execute from pc until a barrier (returns its pc + 1) or the end (None)."""
         while pc < len(self.prog):
-            if wave == 0 and pc in self.body_at:
-                self.bodies_run.append(self.body_at[pc])
+            if pc in self.body_at:
+                self.bodies_by_wave.setdefault(wave, []).append(self.body_at[pc])
+                if wave == 0:
+                    self.bodies_run.append(self.body_at[pc])
             op, args, off = self.prog[pc]
             pc += 1
             if op in ("s_nop", "s_waitcnt"):
@@ -223,7 +226,8 @@ class Program:
             elif op.startswith("s_cmp_"):
                 a, b = m.sval(args[0]), m.sval(args[1])
                 m.scc = int({"s_cmp_eq_u32": a == b, "s_cmp_lg_u32": a != b,
-                             "s_cmp_ge_u32": a >= b, "s_cmp_lt_u32": a < b}[op])
+                             "s_cmp_ge_u32": a >= b, "s_cmp_lt_u32": a < b,
+                             "s_cmp_gt_u32": a > b}[op])
             elif op == "s_add_u32":
                 t = m.sval(args[1]) + m.sval(args[2])
                 m.scc = int(t > 0xFFFFFFFF)

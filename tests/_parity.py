@@ -7,7 +7,9 @@ Tolerances (absolute, per output tensor, over all compared elements):
 LSE is held to the same bounds.  Rows whose oracle LSE is -inf (no visible
 key) must be -inf on the GPU too and have O == 0 exactly.  Grouped K/V heads
 widen the max bound of the summed dK, dV by sqrt(heads per group); the mean
-bound stays.
+bound stays.  Inputs built outside the i.i.d. N(0, 1) recipe to drive nearly
+one-hot attention (keys scaled up) give outputs of V's full magnitude; there
+the max bound scales with max |O_ref| / 2, since bf16 rounding is relative.
 """
 import sys
 
@@ -57,11 +59,13 @@ class Stats:
 
     def __init__(self, name):
         self.name, self.max, self.sum, self.n, self.nan = name, 0.0, 0.0, 0, False
+        self.refmax = 0.0   # largest |reference| seen
 
     def add(self, gpu, ref):
         g = to64(gpu) if torch.is_tensor(gpu) else np.asarray(gpu, dtype=np.float64)
         e = np.abs(g - ref)
         if e.size:
+            self.refmax = max(self.refmax, float(np.nanmax(np.abs(ref))))
             self.nan |= bool(np.isnan(e).any())
             self.max = max(self.max, float(np.nanmax(e)) if not np.isnan(e).all() else 0.0)
             self.sum += float(np.nansum(e))

@@ -34,7 +34,8 @@ def load_gen(d):
 
 
 GENS = {d: load_gen(d) for d in (128, 64)}
-PROGRAMS = {d: Program(G.generate(), ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"), "FA_SLOW")
+PROGRAMS = {d: Program(G.generate(), ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN", "FA_IDLEA",
+                                      "FA_IDLEB"), "FA_SLOW")
             for d, G in GENS.items()}
 
 
@@ -132,6 +133,7 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale, D=128):
         m.s[G.S_VTAILJ] = nt - 2 if tail and nt >= 2 else 0xFFFFFFFF
         m.s[G.S_FM] = fm
         m.s[G.S_FAST] = max(0, min(fm - 1, (nt - 1 if tail else tend) - 2))
+        m.s[G.S_WDIAG] = wave_last_tile(N, q0, w, tend, causal)
         m.s[G.S_J] = 0
         waves.append(m)
     PROGRAM.run_workgroup(waves, lds, mem)
@@ -170,10 +172,16 @@ CASES = [
 ]
 
 
-def expected_bodies(N, q0, causal):
-    """Which body each tile step should take: straight while the next tile is
-    unmasked and both loads are whole tiles, the masked body when the next
-    tile needs a mask, the general one otherwise, the final one last."""
+def wave_last_tile(N, q0, w, tend, causal):
+    """The last tile holding a key wave w sees (the kernel's formula)."""
+    return min(tend - 1, min(q0 + 64 * w + 63, N - 1) // BC) if causal else tend - 1
+
+
+def expected_bodies(N, q0, causal, w=0):
+    """Which body each tile step of wave w should take: straight while the
+    next tile is unmasked and both loads are whole tiles, the masked body
+    when the next tile needs a mask, the general one otherwise, the final
+    one last; idle past the wave's last visible tile."""
     nt = -(-N // BC)
     qmax = min(q0 + BR, N) - 1
     tend = min(nt, qmax // BC + 1) if causal else nt
@@ -183,17 +191,20 @@ def expected_bodies(N, q0, causal):
         fm = min(fm, q0 // BC)
     if ragged:
         fm = min(fm, nt - 1)
+    last = wave_last_tile(N, q0, w, tend, causal)
     out = []
     for j in range(tend - 1):
         k_whole = j + 2 < tend and not (ragged and j + 2 == nt - 1)
         v_whole = not (ragged and j + 1 == nt - 1)
-        if j + 1 >= fm:
+        if j > last:
+            out.append("IDLE")
+        elif j + 1 >= fm:
             out.append("ITM")
         elif k_whole and v_whole:
             out.append("BODY")
         else:
             out.append("GB")
-    return out + ["FIN"]
+    return out + ["IDLE" if tend - 1 > last else "FIN"]
 
 
 @pytest.mark.parametrize("D", [128, 64])
@@ -208,8 +219,11 @@ def test_generated_loop_matches_the_oracle(N, q0, causal, kscale, D):
     scale = D ** -0.5
     PROGRAM.slow_taken = 0
     PROGRAM.bodies_run.clear()
+    PROGRAM.bodies_by_wave.clear()
     O, L = emulate_workgroup(q, k, v, N, q0, causal, scale, D)
-    assert [b[3:] for b in PROGRAM.bodies_run] == expected_bodies(N, q0, causal), PROGRAM.bodies_run
+    for w in range(4):
+        got = [b[3:7] if b.startswith("FA_IDLE") else b[3:] for b in PROGRAM.bodies_by_wave[w]]
+        assert got == expected_bodies(N, q0, causal, w), (w, got)
     # keys scaled by 3 from key 192 on lift those tiles' weights far past 2^8
     # above the reference set by tile 0: the exact slow path must run there
     assert (PROGRAM.slow_taken > 0) == (kscale != 1.0), PROGRAM.slow_taken

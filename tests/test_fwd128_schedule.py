@@ -161,7 +161,7 @@ def follow(lines, env):
         if op.startswith("s_cmp_"):
             x, y = (env[int(t[1:])] if t.startswith("s") else int(t, 0) for t in args[:2])
             scc = {"s_cmp_eq_u32": x == y, "s_cmp_lg_u32": x != y, "s_cmp_ge_u32": x >= y,
-                   "s_cmp_lt_u32": x < y}[op]
+                   "s_cmp_lt_u32": x < y, "s_cmp_gt_u32": x > y}[op]
         elif op in ("s_cbranch_scc0", "s_cbranch_scc1"):
             assert scc is not None, l
             if scc == (op == "s_cbranch_scc1"):
@@ -194,7 +194,7 @@ def load_cases(G):
 
 def env_of(L, case):
     G = L.G
-    return {**load_cases(G)[case], G.S_J: 5, G.S_FAST: 0}
+    return {**load_cases(G)[case], G.S_J: 5, G.S_FAST: 0, G.S_LAST: 11}
 
 
 def stage_tiles(L, lines, ktile, vtile, tail_offs=None):
@@ -339,8 +339,15 @@ BODY_CASES = {"A": ["whole"], "B": ["whole"], "GA": ["whole", "ktail", "kskip"],
               "FA": ["whole"], "FB": ["whole"]}
 
 
+# idle steps (a wave past its last visible tile): loads and the barrier only
+IDLE = {"IA": ("FA_IDLEA_%=:", None, None, 0, 1, False),
+        "IB": ("FA_IDLEB_%=:", None, None, 1, 0, False)}
+BODY_CASES.update({"IA": ALL_CASES, "IB": ALL_CASES})
+
+
 def body_of(L, name):
-    return L.section(BODIES[name][0], "s_barrier")
+    label = (BODIES.get(name) or IDLE[name])[0]
+    return L.section(label, "s_barrier")
 
 
 @pytest.mark.parametrize("d", DIMS)
@@ -376,7 +383,8 @@ def tail_offsets(L, N, tlast):
 
 
 @pytest.mark.parametrize("d", DIMS)
-@pytest.mark.parametrize("name,case", [(n, c) for n in BODIES for c in BODY_CASES[n]])
+@pytest.mark.parametrize("name,case", [(n, c) for n in list(BODIES) + list(IDLE)
+                                       for c in BODY_CASES[n]])
 def test_direct_loads_place_tiles_as_the_reads_expect(name, case, d):
     """The emitted loads (M0 values, offset registers, instruction offsets)
     write chunk q of tile row r to slot q ^ swz(r) of the right stage, for
@@ -385,7 +393,7 @@ def test_direct_loads_place_tiles_as_the_reads_expect(name, case, d):
     repeating the last one; a tile past the end is not loaded."""
     L = LOOPS[d]
     D = L.D
-    _, _, _, kst, vst, final = BODIES[name]
+    _, _, _, kst, vst, final = (BODIES.get(name) or IDLE[name])
     N, tlast = 3 * 64 + 37, 3
     ktile = np.arange(64 * D).reshape(64, D) + 10 ** 6
     vtile = np.arange(64 * D).reshape(64, D) + 2 * 10 ** 6
@@ -622,9 +630,10 @@ def test_every_barrier_waits_for_the_direct_loads(d):
 
 
 @pytest.mark.parametrize("d", DIMS)
-@pytest.mark.parametrize("path", range(NPATHS))
+@pytest.mark.parametrize("path", range(NPATHS + 8))
 def test_m0_set_at_least_one_state_before_each_direct_load(path, d):
-    body = PATHS[d][path]
+    idle = [follow(body_of(LOOPS[d], n), env_of(LOOPS[d], c)) for n in IDLE for c in ALL_CASES]
+    body = (PATHS[d] + idle)[path]
     last_m0 = None
     for i, l in enumerate(body):
         if l.startswith("s_add_u32 m0,"):
@@ -650,11 +659,16 @@ def test_straight_body_keeps_its_branch_condition(d):
 
 
 # ------------------------------------------------------------ tile counts
-def run_control(L, N, q0, causal):
+def wave_last_tile(N, q0, w, tend, causal):
+    """The last tile holding a key wave w sees (the kernel's formula)."""
+    return min(tend - 1, min(q0 + 64 * w + 63, N - 1) // 64) if causal else tend - 1
+
+
+def run_control(L, N, q0, causal, w=0):
     """Execute the scalar part of the whole statement with the kernel's
-    start values (no slow path): which K and V tiles get loaded (and whether
-    through the clamped offsets), which tiles get masked, which body each
-    step takes."""
+    start values for wave w (no slow path): which K and V tiles get loaded
+    (and whether through the clamped offsets), which tiles get masked, which
+    body each step takes, how many barriers the wave meets."""
     G, LINES = L.G, L.LINES
     BC, BR = 64, 256
     nt = -(-N // BC)
@@ -673,11 +687,12 @@ def run_control(L, N, q0, causal):
     s = {G.S_LAST: tend - 1, G.S_KEND: max(0, tend - 2),
          G.S_KTAILJ: nt - 3 if tail and nt >= 3 else NONE,
          G.S_VTAILJ: nt - 2 if tail and nt >= 2 else NONE,
-         G.S_FM: fm, G.S_FAST: max(0, min(fm - 1, kfull - 2)), G.S_J: 0}
+         G.S_FM: fm, G.S_FAST: max(0, min(fm - 1, kfull - 2)), G.S_J: 0,
+         G.S_WDIAG: wave_last_tile(N, q0, w, tend, causal)}
     ptr = {G.S_KPTR: KB + 2 * TB, G.S_VPTR: VB + TB}
     kload = [(0, False)] + ([(1, False)] if tend > 1 else [])   # the C++ prologue's
     vload = [(0, False)]
-    masked, bodies = [], []
+    masked, bodies, barriers = [], [], 0
     labels = {l[:-1]: i for i, l in enumerate(LINES) if l.endswith(":")}
     pc, scc, steps = 0, None, 0
     while True:
@@ -687,18 +702,20 @@ def run_control(L, N, q0, causal):
         pc += 1
         if l == "FA_DONE_%=:":
             break
-        for kind in ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN"):
+        for kind in ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN", "FA_IDLEA", "FA_IDLEB"):
             if l.startswith(kind) and l.endswith(":"):
-                bodies.append(kind[3:])
+                bodies.append(kind[3:7] if kind.startswith("FA_IDLE") else kind[3:])
                 if kind == "FA_ITM":
                     masked.append(s[G.S_J] + 1)
+        if l == "s_barrier":
+            barriers += 1
         if l == "s_cbranch_scc1 FA_EMASK_%=" and s[G.S_FM] == 0:
             masked.append(0)
         op, args = split(l)
         if op.startswith("s_cmp_"):
             x, y = (s[int(t[1:])] if t.startswith("s") else int(t, 0) for t in args[:2])
             scc = {"s_cmp_eq_u32": x == y, "s_cmp_lg_u32": x != y, "s_cmp_ge_u32": x >= y,
-                   "s_cmp_lt_u32": x < y}[op]
+                   "s_cmp_lt_u32": x < y, "s_cmp_gt_u32": x > y}[op]
         elif op in ("s_cbranch_scc0", "s_cbranch_scc1"):
             if scc == (op == "s_cbranch_scc1"):
                 pc = labels[args[0]]
@@ -716,7 +733,7 @@ def run_control(L, N, q0, causal):
                 t = (p - (KB if is_k else VB)) // TB
                 assert 0 <= t < nt, (N, q0, t)
                 (kload if is_k else vload).append((t, reg == G.GOFF_TAIL))
-    return tend, fm, kload, vload, masked, bodies
+    return tend, fm, kload, vload, masked, bodies, barriers
 
 
 @pytest.mark.parametrize("d", DIMS)
@@ -724,22 +741,35 @@ def run_control(L, N, q0, causal):
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 200, 256, 300, 511, 512,
                                700, 1000, 1024, 8192])
 def test_loop_loads_and_masks(N, causal, d):
-    """Every tile in [0, tend) is loaded once, in order, whole tiles through
-    the plain offsets and only a partial last tile through the clamped ones;
-    exactly the tiles that hold an invisible key are masked; every step
-    before the last takes the straight body when its next tile is unmasked
-    and both its loads are whole tiles."""
+    """For every wave: every tile in [0, tend) is loaded once, in order, whole
+    tiles through the plain offsets and only a partial last tile through the
+    clamped ones; exactly the tiles that hold an invisible key are masked, up
+    to the one after the wave's last visible tile; every step before the
+    last takes the straight body when its next tile is unmasked and both its
+    loads are whole tiles, and steps past the wave's last visible tile are
+    idle (never a straight one); all four waves meet the same barriers."""
     for q0 in range(0, N, 256):
-        tend, fm, kload, vload, masked, bodies = run_control(LOOPS[d], N, q0, causal)
-        assert [t for t, _ in kload] == list(range(tend))
-        assert [t for t, _ in vload] == list(range(tend))
-        for t, clamped in kload[2:] + vload[1:]:
-            assert clamped == (t * 64 + 63 >= N)
-        need = [t for t in range(tend)
-                if t * 64 + 63 >= N or (causal and t * 64 + 63 > q0)]
-        assert masked == need, (N, q0, masked, need)
-        want = []
-        for j in range(tend - 1):
-            whole = j + 2 < tend and (j + 2) * 64 + 63 < N and (j + 1) * 64 + 63 < N
-            want.append("ITM" if j + 1 in need else "BODY" if whole else "GB")
-        assert bodies == want + ["FIN"], (N, q0, bodies, want)
+        nbar = set()
+        for w in range(4):
+            tend, fm, kload, vload, masked, bodies, barriers = run_control(LOOPS[d], N, q0,
+                                                                           causal, w)
+            nbar.add(barriers)
+            last = wave_last_tile(N, q0, w, tend, causal)
+            assert [t for t, _ in kload] == list(range(tend))
+            assert [t for t, _ in vload] == list(range(tend))
+            for t, clamped in kload[2:] + vload[1:]:
+                assert clamped == (t * 64 + 63 >= N)
+            need = [t for t in range(tend)
+                    if t * 64 + 63 >= N or (causal and t * 64 + 63 > q0)]
+            need = [t for t in need if t == 0 or t - 1 <= last]
+            assert masked == need, (N, q0, w, masked, need)
+            want = []
+            for j in range(tend - 1):
+                whole = j + 2 < tend and (j + 2) * 64 + 63 < N and (j + 1) * 64 + 63 < N
+                if j > last:
+                    want.append("IDLE")
+                else:
+                    want.append("ITM" if j + 1 in need else "BODY" if whole else "GB")
+            want.append("IDLE" if tend - 1 > last else "FIN")
+            assert bodies == want, (N, q0, w, bodies, want)
+        assert len(nbar) == 1, (N, q0, nbar)

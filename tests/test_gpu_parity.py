@@ -68,9 +68,10 @@ def nan_bwd_out(q, k):
             torch.full(k.shape, NAN, dtype=torch.float32, device=DEV))
 
 
-def forward_parity_all_heads(q, k, v, causal, mask=None, chunk=8):
+def forward_parity_all_heads(q, k, v, causal, mask=None, chunk=8, magnitude_scaled=False):
     """The whole forward output (every head, row and column) against the
-    oracle, written over NaN-filled buffers."""
+    oracle, written over NaN-filled buffers.  magnitude_scaled: the max bound
+    of O scales with max |O_ref| / 2 (inputs outside the i.i.d. recipe)."""
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     out = nan_fwd_out(qd)
     if mask is None:
@@ -88,7 +89,7 @@ def forward_parity_all_heads(q, k, v, causal, mask=None, chunk=8):
                                 mask_block=128)
         so.add(heads_of(o, pc), ro)
         check_lse(torch.stack([lse[b, h] for b, h in pc]), rl, stats=sl)
-    so.check()
+    so.check(max_scale=max(1.0, so.refmax / 2) if magnitude_scaled else 1.0)
     sl.check()
     return o, lse
 
@@ -203,14 +204,17 @@ def test_forward_reference_moves_mid_sequence(N, causal, d):
     than 2^3 per weight: the hand-scheduled loop must take its exact path
     (row maximum, rescale, recomputed weights) there, in the launch
     configuration of the long workloads (B2 H130: more than one 256-row
-    workgroup per CU)."""
+    workgroup per CU).  Such keys make the attention nearly one-hot, so O
+    reaches V's magnitude (|O| up to about 4.3, where one bf16 ulp is
+    2^-6 and rounding O alone costs 7.8e-3): the max bound of O scales with
+    max |O_ref| / 2."""
     need_gpu()
     log(f"forward bf16 B2 H130 N{N} d{d} causal={causal}, keys x3 from key 192 on")
     q, k, v = inputs.qkv(2, 130, N, d, torch.bfloat16, seed=2000 + N + d)
     kscale = torch.ones(N, dtype=torch.float32)
     kscale[192:] = 3.0
     k = (k.float() * kscale[None, None, :, None]).to(torch.bfloat16)
-    forward_parity_all_heads(q, k, v, causal, chunk=65)
+    forward_parity_all_heads(q, k, v, causal, chunk=65, magnitude_scaled=True)
 
 
 def test_caller_outputs_match_fresh_outputs():
