@@ -323,69 +323,12 @@ def products(st, lds, units, lv, valu, raw_sched=None, pre=0, nxt=None):
         stg, half, x = lv
         for i, rd in enumerate(lv_reads(stg, half, x)):
             sched.setdefault(min(2 * i + 1, len(mf) - LEAD - 1), []).append(rd)
-    interleave_even(st, mf, before, valu, lds, sched, need, raw_sched=raw_sched)
+    F.interleave_even(st, mf, before, valu, lds, sched, need, raw_sched=raw_sched, gap=GAP,
+                      init=INIT)
 
 
 GAP = 28.0        # most issue cycles of other work between two products
 INIT = 0.0        # vector work before the first product of a call
-
-
-def interleave_even(st, mfmas, reads_before, valu, lds, read_sched, operand_reads,
-                    raw_sched=None):
-    """Emit the products in order; after product i the LDS reads scheduled
-    for it, the scalar/load lines raw_sched[i], then vector work.  Unlike
-    the forward's filler, which packs each product's shadow full, the
-    vector work is spread evenly: after product i it takes the remaining
-    work's share of the remaining products (at most GAP cycles with the
-    reads and scalar lines), so the matrix pipe never waits on a burst and
-    no work is left for the end.  A product waits (s_waitcnt) until its
-    operand reads have landed."""
-    raw_sched = raw_sched or {}
-    valu = list(valu)
-
-    def ready(i):
-        ins = valu[i]
-        if st.need(ins) > 0:
-            return False
-        for prev in valu[:i]:
-            if (ins.uses | ins.srcc) & prev.defs or ins.defs & (prev.uses | prev.srcc | prev.defs):
-                return False
-        return True
-
-    def fill(budget):
-        used = 0.0
-        while valu:
-            pick = next((i for i in range(min(F.LOOKAHEAD, len(valu))) if ready(i)), None)
-            if pick is None or used + valu[pick].cost > budget + 1e-9:
-                break
-            ins = valu.pop(pick)
-            st.emit(ins)
-            used += ins.cost
-
-    for rid, ins in reads_before:
-        st.emit(ins)
-        lds.issue(rid)
-    if mfmas and INIT:
-        fill(INIT)
-    n = len(mfmas)
-    for i, mf in enumerate(mfmas):
-        k = lds.wait_for(operand_reads[i])
-        if k is not None:
-            st.raw(f"s_waitcnt lgkmcnt({min(k, 15)})")
-        st.emit(mf)
-        spent = 0.0
-        for rid, ins in read_sched.get(i, []):
-            st.emit(ins)
-            lds.issue(rid)
-            spent += ins.cost
-        for line in raw_sched.get(i, []):
-            st.raw(line)
-            spent += F.COST["vmem"] if line.startswith("global_") else F.COST["salu"]
-        left = sum(x.cost for x in valu)
-        share = left / max(1, n - i)
-        fill(min(GAP - spent, share + 4.5))
-    for ins in valu:
-        st.emit(ins)
 
 
 def end_step(st, lds, last):

@@ -90,6 +90,8 @@ V_STAGE0 = 65536            # V stage s at 64 KiB + 16 KiB s
 TILE_BYTES = 64 * 256
 
 H_SRC_WAR = 12    # product reading a register as A/B -> vector write of it
+GAP = 24.0        # most issue cycles of other work between two products (the
+                  # vector work is spread evenly over a step's products)
 
 
 class Stream(F.Stream):
@@ -289,7 +291,7 @@ def products(st, lds, sdp, dq, valu, raw_sched=None, pre_t=None):
                 at = n0 + 2 * (o - AHEAD)
                 sched.setdefault(at, []).extend([(("T", o, hi), reads[hi]) for hi in range(2)])
     need = {i: need.get(i, set()) for i in range(len(mf))}
-    F.interleave(st, mf, before, valu, lds, sched, need, raw_sched=raw_sched)
+    F.interleave_even(st, mf, before, valu, lds, sched, need, raw_sched=raw_sched, gap=GAP)
 
 
 def full_loads(which, stage_off):

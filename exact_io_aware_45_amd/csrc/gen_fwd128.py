@@ -547,6 +547,64 @@ def interleave(st, mfmas, reads_before, valu, lds, read_sched, operand_reads, ta
     return valu
 
 
+def interleave_even(st, mfmas, reads_before, valu, lds, read_sched, operand_reads,
+                    raw_sched=None, gap=28.0, init=0.0):
+    """Emit the products in order; after product i the LDS reads scheduled
+    for it, the scalar/load lines raw_sched[i], then vector work.  Unlike
+    the forward's filler, which packs each product's shadow full, the
+    vector work is spread evenly: after product i it takes the remaining
+    work's share of the remaining products (at most `gap` cycles with the
+    reads and scalar lines), so the matrix pipe never waits on a burst and
+    no work is left for the end.  A product waits (s_waitcnt) until its
+    operand reads have landed."""
+    raw_sched = raw_sched or {}
+    valu = list(valu)
+
+    def ready(i):
+        ins = valu[i]
+        if st.need(ins) > 0:
+            return False
+        for prev in valu[:i]:
+            if (ins.uses | ins.srcc) & prev.defs or ins.defs & (prev.uses | prev.srcc | prev.defs):
+                return False
+        return True
+
+    def fill(budget):
+        used = 0.0
+        while valu:
+            pick = next((i for i in range(min(LOOKAHEAD, len(valu))) if ready(i)), None)
+            if pick is None or used + valu[pick].cost > budget + 1e-9:
+                break
+            ins = valu.pop(pick)
+            st.emit(ins)
+            used += ins.cost
+
+    for rid, ins in reads_before:
+        st.emit(ins)
+        lds.issue(rid)
+    if mfmas and init:
+        fill(init)
+    n = len(mfmas)
+    for i, mf in enumerate(mfmas):
+        k = lds.wait_for(operand_reads[i])
+        if k is not None:
+            st.raw(f"s_waitcnt lgkmcnt({min(k, 15)})")
+        st.emit(mf)
+        spent = 0.0
+        for rid, ins in read_sched.get(i, []):
+            st.emit(ins)
+            lds.issue(rid)
+            spent += ins.cost
+        for line in raw_sched.get(i, []):
+            st.raw(line)
+            spent += COST["vmem"] if line.startswith("global_") else COST["salu"]
+        left = sum(x.cost for x in valu)
+        share = left / max(1, n - i)
+        fill(min(gap - spent, share + 4.5))
+    for ins in valu:
+        st.emit(ins)
+
+
 def phase_a(st, lds, cur, pcur, nxt, kstage, final, tmp_ring, raw_sched=None):
     """Scores of the next tile (4 NC products) beside the second half of the
     current tile's weights, then the sum test.  Returns the tile-sum regs."""
