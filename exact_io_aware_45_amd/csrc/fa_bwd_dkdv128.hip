@@ -1,8 +1,7 @@
 // fa_bwd_dkdv128.hip -- the dK/dV pass of the backward for head dim 128, bf16
 // inputs, fp32 dK and dV, with a hand-scheduled query loop (gfx950).
 //
-// Same result as bwd_dkdv_split_kernel (fa_bwd.hip) when every query head
-// has its own K/V head: for every key the scores and their gradient are
+// Same result as bwd_dkdv_split_kernel (fa_bwd.hip): for every key the scores and their gradient are
 // recomputed tile by tile from the saved log-sum-exp, never stored
 // ("FlashAttention." plate, "Never write the scores"), and
 //   dV = sum_i P_i^T dO_i,  dK = scale * sum_i dS_i^T Q_i,
@@ -12,11 +11,15 @@
 // dP product chain, so the products leave dP - D).
 //
 // Work decomposition:
-//   * one workgroup = 4 waves = 128 keys of one head, one resident workgroup
-//     per CU taking 128-key items in turn (fa_resident.hpp; with a causal
-//     mask the first key blocks, which see the most queries, go first); each
-//     wave owns 32 keys: their K and V rows and their dK^T, dV^T
+//   * one workgroup = 4 waves = 128 keys of one K/V head, one resident
+//     workgroup per CU taking 128-key items in turn (fa_resident.hpp; with a
+//     causal mask the first key blocks, which see the most queries, go
+//     first); each wave owns 32 keys: their K and V rows and their dK^T, dV^T
 //     accumulators sit in the accumulation registers;
+//   * with grouped K/V heads the item runs the query loop once per query
+//     head of its group (or of its slice of the group: then it writes fp32
+//     partial sums that bwd_dkv_reduce_kernel adds in slot order), the
+//     accumulators passed on from one run to the next;
 //   * Q and dO tiles (64 queries) load three tiles ahead, HBM -> LDS by
 //     direct loads, into four stages each (a tile is read as rows for the
 //     scores and, half a tile later, transposed for the gradients), and each
@@ -58,25 +61,36 @@ void bwd_dkdv128_kernel(BwdArgs a) {
   auto lds_base = [&]() {
     return fresh(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS bf16*)smem)));
   };
-  auto shape = [&]() { return fresh_shape<BK, BQ>(a.N, a.B, a.H, a.Hkv); };
+  // Items: 128-key blocks of each (K/V head, slice of its query heads).
+  auto shape = [&]() { return fresh_shape<BK, BQ>(a.N, a.B, a.Hkv * a.gsplit, a.Hkv); };
   // Key block of an item: with a causal mask, item rank 0 (handed out first)
   // is key block 0, which sees every query.
   auto key0_of = [&](const Shape& sh, const Item& it) {
     return CAUSAL ? (sh.nq - 1) * BK - it.q0 : it.q0;
   };
-  // The item's query tiles ts .. ts + 2 into stages 0 .. 2, and this wave's
-  // copy of their L and D values (the LDS they fill is free: the previous
-  // item's loop and epilogue ended with a barrier after their last read).
-  auto dma_first_tiles = [&](const Shape& sh, const Item& it) {
+  // Query head g of an item's (K/V head, slice): the group of K/V head
+  // b Hkv + j is query heads b H + j H/Hkv .. + H/Hkv - 1, split in gsplit
+  // slices of consecutive heads.
+  auto qhead_of = [&](const Item& it, int g) {
+    const int H = fresh(a.H), Hkv = fresh(a.Hkv), gs = fresh(a.gsplit);
+    const int kvh = it.bh / gs, slice = it.bh % gs;
+    const int G = H / Hkv;
+    return (kvh / Hkv) * H + (kvh % Hkv) * G + slice * (G / gs) + g;
+  };
+  // Query head bq's tiles ts .. ts + 2 of the item into stages 0 .. 2, and
+  // this wave's copy of their L and D values (the LDS they fill is free: the
+  // statement before, or the previous item's epilogue, ended with a barrier
+  // after their last read).
+  auto dma_first_tiles = [&](const Shape& sh, const Item& it, int bq) {
     const int wave = fresh(wave0);
     const uint32_t lds0 = lds_base();
     const int ts = CAUSAL ? key0_of(sh, it) / BQ : 0;
     const int cnt = sh.nt - ts;
-    const size_t head = (size_t)it.bh * (size_t)sh.N * D;
+    const size_t head = (size_t)bq * (size_t)sh.N * D;
     const bf16* Q = fresh(reinterpret_cast<const bf16*>(a.q)) + head;
     const bf16* dO = fresh(reinterpret_cast<const bf16*>(a.dout)) + head;
-    const float* lse2 = fresh(a.lse2) + (size_t)it.bh * sh.N;
-    const float* del = fresh(a.delta) + (size_t)it.bh * sh.N;
+    const float* lse2 = fresh(a.lse2) + (size_t)bq * sh.N;
+    const float* del = fresh(a.delta) + (size_t)bq * sh.N;
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       if (s < cnt) {
@@ -88,46 +102,23 @@ void bwd_dkdv128_kernel(BwdArgs a) {
     }
   };
 
-  Item cur;
-  {
+  // One run of the query loop: query head bq's tiles against the item's keys,
+  // added to dk, dv.  Every per-lane value is derived here again, so that
+  // nothing but the item, the accumulators and the K/V rows lives across the
+  // statement, which overwrites most registers.
+  auto run_query_loop = [&](const Item& it, int bq, f32x16 (&dk)[4], f32x16 (&dv)[4],
+                            bf16x8 (&kf)[8], bf16x8 (&vf)[8]) {
     const Shape sh = shape();
-    if (!resident_item<CAUSAL, BK>(sh, 0, cur)) return;
-    dma_first_tiles(sh, cur);
-  }
-
-  for (int r = 0;; ++r) {
-    const Shape sh = shape();
-    Item nxt;
-    const bool more = resident_item<CAUSAL, BK>(sh, r + 1, nxt);
     const int N = sh.N, nt = sh.nt;
     const int wave = fresh(wave0);
     const uint32_t lds0 = lds_base();
-    const int k0 = key0_of(sh, cur);
-    const int ts = CAUSAL ? k0 / BQ : 0;   // first query tile that sees a key of the block
-    const int cnt = nt - ts;               // query tiles of the item
-    const size_t head = (size_t)cur.bh * (size_t)N * D;
-    const bf16* __restrict__ Q = fresh(reinterpret_cast<const bf16*>(a.q)) + head;
-    const bf16* __restrict__ dO = fresh(reinterpret_cast<const bf16*>(a.dout)) + head;
-    const float* lse2 = fresh(a.lse2) + (size_t)cur.bh * N;
-    const float* del = fresh(a.delta) + (size_t)cur.bh * N;
-
-    // This wave's K and V rows: lane (l32, h) holds key k0 + 32 wave + l32,
-    // d = 16 c + 8 h .. +7 (keys past the sequence repeat its last one; their
-    // dK and dV are never stored).
+    const int k0 = key0_of(sh, it);
+    const int ts = CAUSAL ? k0 / BQ : 0;
+    const int cnt = nt - ts;
     const int lane = fresh_lane();
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const int key = k0 + 32 * wave + l32;
-    const size_t krow = head + (size_t)min(key, N - 1) * D;
-    const bf16* Kr = fresh(reinterpret_cast<const bf16*>(a.k)) + krow + 8 * h;
-    const bf16* Vr = fresh(reinterpret_cast<const bf16*>(a.v)) + krow + 8 * h;
-    bf16x8 kf[8], vf[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      kf[c] = *reinterpret_cast<const bf16x8*>(Kr + 16 * c);
-      vf[c] = *reinterpret_cast<const bf16x8*>(Vr + 16 * c);
-    }
-
     // Lane parts of the LDS operand addresses (byte addresses in Q stage 0
     // and dO stage 0, first 32-query half).
     const int sw_row = tile_swz<D>(l32);
@@ -183,11 +174,6 @@ void bwd_dkdv128_kernel(BwdArgs a) {
     const uint32_t m0o = uni(lds0 + OST0 + wave * 4096);
     const uint32_t m0l = uni(lds0 + LST0 + wave * 512);
     const uint32_t cbits = uniform_bits(fresh(a.scale) * kLog2e);   // scale * log2(e)
-    uint64_t qptr = uni64(reinterpret_cast<uint64_t>(Q + (size_t)(ts + 3) * TILE));
-    uint64_t optr = uni64(reinterpret_cast<uint64_t>(dO + (size_t)(ts + 3) * TILE));
-    uint64_t lptr = uni64(reinterpret_cast<uint64_t>(lse2 + (size_t)(ts + 3) * BQ));
-    // The D load carries instruction offset 256 (its LDS area follows L's).
-    uint64_t dptr = uni64(reinterpret_cast<uint64_t>(del + (size_t)(ts + 3) * BQ) - 256u);
     // Loop control, in tiles relative to ts: step j processes tile j and
     // loads tile j + 3; the partial last tile (loaded by step cnt - 4) goes
     // through the clamped offsets; tiles below `mlo` (the causal diagonal) and
@@ -204,23 +190,35 @@ void bwd_dkdv128_kernel(BwdArgs a) {
     const uint32_t sfast = uni((uint32_t)max(0, mhi - 3));
     const uint32_t smask0 = uni((mlo > 0 || mhi == 0) ? 1u : 0u);
     const float ninf = -INFINITY;
+
+    const size_t head = (size_t)bq * (size_t)N * D;
+    const bf16* Q = fresh(reinterpret_cast<const bf16*>(a.q)) + head;
+    const bf16* dO = fresh(reinterpret_cast<const bf16*>(a.dout)) + head;
+    const float* lse2 = fresh(a.lse2) + (size_t)bq * N;
+    const float* del = fresh(a.delta) + (size_t)bq * N;
+    uint64_t qptr = uni64(reinterpret_cast<uint64_t>(Q + (size_t)(ts + 3) * TILE));
+    uint64_t optr = uni64(reinterpret_cast<uint64_t>(dO + (size_t)(ts + 3) * TILE));
+    uint64_t lptr = uni64(reinterpret_cast<uint64_t>(lse2 + (size_t)(ts + 3) * BQ));
+    // The D load carries instruction offset 256 (its LDS area follows L's).
+    uint64_t dptr = uni64(reinterpret_cast<uint64_t>(del + (size_t)(ts + 3) * BQ) - 256u);
     wait_vmem();
     __syncthreads();   // tiles 0 .. 2 are in LDS for every wave
 
-    f32x16 dk[4], dv[4];
     asm volatile(FA_BWD_DKDV128_LOOP_ASM
-                 : "={a[0:15]}"(dk[0]), "={a[16:31]}"(dk[1]), "={a[32:47]}"(dk[2]),
-                   "={a[48:63]}"(dk[3]), "={a[64:79]}"(dv[0]), "={a[80:95]}"(dv[1]),
-                   "={a[96:111]}"(dv[2]), "={a[112:127]}"(dv[3]),
+                 : "+{a[0:15]}"(dk[0]), "+{a[16:31]}"(dk[1]), "+{a[32:47]}"(dk[2]),
+                   "+{a[48:63]}"(dk[3]), "+{a[64:79]}"(dv[0]), "+{a[80:95]}"(dv[1]),
+                   "+{a[96:111]}"(dv[2]), "+{a[112:127]}"(dv[3]),
                    "+{s[60:61]}"(qptr), "+{s[62:63]}"(optr), "+{s[84:85]}"(lptr),
-                   "+{s[86:87]}"(dptr), "+{s71}"(jt)
-                 : "{a[128:131]}"(kf[0]), "{a[132:135]}"(kf[1]), "{a[136:139]}"(kf[2]),
-                   "{a[140:143]}"(kf[3]), "{a[144:147]}"(kf[4]), "{a[148:151]}"(kf[5]),
-                   "{a[152:155]}"(kf[6]), "{a[156:159]}"(kf[7]),
-                   "{a[160:163]}"(vf[0]), "{a[164:167]}"(vf[1]), "{a[168:171]}"(vf[2]),
-                   "{a[172:175]}"(vf[3]), "{a[176:179]}"(vf[4]), "{a[180:183]}"(vf[5]),
-                   "{a[184:187]}"(vf[6]), "{a[188:191]}"(vf[7]),
-                   "{v[160:167]}"(raddr), "{v[168:175]}"(draddr), "{v[176:183]}"(taddr),
+                   "+{s[86:87]}"(dptr), "+{s71}"(jt),
+                   // unchanged by the statement; in-out so that they stay in
+                   // place from one run to the next
+                   "+{a[128:131]}"(kf[0]), "+{a[132:135]}"(kf[1]), "+{a[136:139]}"(kf[2]),
+                   "+{a[140:143]}"(kf[3]), "+{a[144:147]}"(kf[4]), "+{a[148:151]}"(kf[5]),
+                   "+{a[152:155]}"(kf[6]), "+{a[156:159]}"(kf[7]),
+                   "+{a[160:163]}"(vf[0]), "+{a[164:167]}"(vf[1]), "+{a[168:171]}"(vf[2]),
+                   "+{a[172:175]}"(vf[3]), "+{a[176:179]}"(vf[4]), "+{a[180:183]}"(vf[5]),
+                   "+{a[184:187]}"(vf[6]), "+{a[188:191]}"(vf[7])
+                 : "{v[160:167]}"(raddr), "{v[168:175]}"(draddr), "{v[176:183]}"(taddr),
                    "{v[184:191]}"(tdaddr), "{v192}"(laddr), "{v[196:199]}"(goff),
                    "{v[200:203]}"(gtail), "{v204}"(loff), "{v205}"(ltail), "{v206}"(ta),
                    "{v207}"(range), "{v208}"(ninf),
@@ -228,6 +226,55 @@ void bwd_dkdv128_kernel(BwdArgs a) {
                    "{s69}"(stailj), "{s70}"(smlo), "{s72}"(smhi), "{s82}"(sfast), "{s88}"(m0l),
                    "{s89}"(smask0)
                  : FA_BWD_DKDV128_LOOP_CLOBBERS);
+  };
+
+  Item cur;
+  {
+    const Shape sh = shape();
+    if (!resident_item<CAUSAL, BK>(sh, 0, cur)) return;
+    dma_first_tiles(sh, cur, qhead_of(cur, 0));
+  }
+
+  for (int r = 0;; ++r) {
+    const Shape sh = shape();
+    Item nxt;
+    const bool more = resident_item<CAUSAL, BK>(sh, r + 1, nxt);
+    const int N = sh.N;
+    const int wave = fresh(wave0);
+    const int k0 = key0_of(sh, cur);
+    const int kvh = cur.bh / fresh(a.gsplit);   // K/V head of the item
+    const size_t kvhead = (size_t)kvh * (size_t)N * D;
+
+    // This wave's K and V rows: lane (l32, h) holds key k0 + 32 wave + l32,
+    // d = 16 c + 8 h .. +7 (keys past the sequence repeat its last one; their
+    // dK and dV are never stored).
+    const int lane = fresh_lane();
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int key = k0 + 32 * wave + l32;
+    const size_t krow = kvhead + (size_t)min(key, N - 1) * D;
+    const bf16* Kr = fresh(reinterpret_cast<const bf16*>(a.k)) + krow + 8 * h;
+    const bf16* Vr = fresh(reinterpret_cast<const bf16*>(a.v)) + krow + 8 * h;
+    bf16x8 kf[8], vf[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      kf[c] = *reinterpret_cast<const bf16x8*>(Kr + 16 * c);
+      vf[c] = *reinterpret_cast<const bf16x8*>(Vr + 16 * c);
+    }
+
+    // The query loop once per query head of the item's group (slice), the
+    // accumulators passed on from one run to the next.
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dk[i][e] = dv[i][e] = 0.f;
+    const int heads = fresh(a.H) / fresh(a.Hkv) / fresh(a.gsplit);
+    for (int g = 0; g < heads; ++g) {
+      // The previous run ended with a barrier after its last LDS read.
+      if (g > 0) dma_first_tiles(shape(), cur, qhead_of(cur, g));
+      run_query_loop(cur, qhead_of(cur, g), dk, dv, kf, vf);
+    }
 
     // Epilogue: dK = scale * acc, dV = acc, fp32.  Lane (l32, h) of block db
     // holds key l32, d = 32 db + 8 g + 4 h .. +3 in registers 4g .. 4g + 3:
@@ -268,12 +315,19 @@ void bwd_dkdv128_kernel(BwdArgs a) {
       rv[i] = *reinterpret_cast<const FA_LDS f32x4*>(stg + 16384 + 512 * row + slot);
     }
     __syncthreads();   // every wave has its rows: the LDS takes the next item's tiles
-    if (more) dma_first_tiles(sh2, nxt);
+    if (more) dma_first_tiles(sh2, nxt, qhead_of(nxt, 0));
     const int kw = key0_of(sh2, cur) + 32 * wave2;
     typedef __attribute__((address_space(1))) f32x4 gf32x4;
-    const size_t row0 = ((size_t)cur.bh * sh2.N + kw + eh) * D + 4 * e32;
-    gf32x4* dkp = (gf32x4*)(fresh(a.dk) + row0);
-    gf32x4* dvp = (gf32x4*)(fresh(a.dv) + row0);
+    // dK, dV of the K/V head, or (slices) partial slots slice and
+    // gsplit + slice of `part`.
+    const int gs2 = fresh(a.gsplit);
+    const int kvh2 = cur.bh / gs2, slice2 = cur.bh % gs2;
+    const size_t kvsize = (size_t)fresh(a.B) * (size_t)fresh(a.Hkv) * (size_t)sh2.N * D;
+    const size_t row0 = ((size_t)kvh2 * sh2.N + kw + eh) * D + 4 * e32;
+    float* dkbase = gs2 > 1 ? fresh(a.part) + (size_t)slice2 * kvsize : fresh(a.dk);
+    float* dvbase = gs2 > 1 ? fresh(a.part) + (size_t)(gs2 + slice2) * kvsize : fresh(a.dv);
+    gf32x4* dkp = (gf32x4*)(dkbase + row0);
+    gf32x4* dvp = (gf32x4*)(dvbase + row0);
     const int rows = sh2.N - kw;   // rows of this wave inside the sequence
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -290,15 +344,16 @@ void bwd_dkdv128_kernel(BwdArgs a) {
 }  // namespace
 
 // Whether the hand-scheduled dK/dV kernel takes this backward: head dim 128,
-// no tile mask, one K/V head per query head, at least one 128-key item per CU.
+// no tile mask, at least one item (128 keys of one K/V head and slice) per
+// CU.
 bool dkdv128_applies(const BwdArgs& a) {
-  if (a.d != 128 || a.mask != nullptr || a.Hkv != a.H || a.gsplit != 1) return false;
-  const long long items = (long long)((a.N + BK - 1) / BK) * a.B * a.H;
+  if (a.d != 128 || a.mask != nullptr) return false;
+  const long long items = (long long)((a.N + BK - 1) / BK) * a.B * a.Hkv * a.gsplit;
   return items >= 256;
 }
 
 hipError_t launch_dkdv128(const BwdArgs& a, hipStream_t s) {
-  const long long items = (long long)((a.N + BK - 1) / BK) * a.B * a.H;
+  const long long items = (long long)((a.N + BK - 1) / BK) * a.B * a.Hkv * a.gsplit;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const long long grid = std::min<long long>(items, resident_cu_count());
   if (a.causal)

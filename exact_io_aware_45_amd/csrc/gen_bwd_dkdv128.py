@@ -461,17 +461,17 @@ def iteration(out, p, kind, name):
 
 
 def entry(out):
-    """Query tile 0: its first half's L/D and S/dP products (dK/dV
-    accumulators cleared beside them), that half's mask when the tile needs
-    one, its vector work beside the second half's S/dP products and L/D
-    reads and the reads of the first step's first gradient products."""
+    """Query tile 0: its first half's L/D and S/dP products, that half's mask
+    when the tile needs one, its vector work beside the second half's S/dP
+    products and L/D reads and the reads of the first step's first gradient
+    products.  The dK/dV accumulators come in holding the sums so far (zero
+    for an item's first query head; with grouped heads the statement runs
+    once per query head of the group)."""
     st = Stream(out)
     st.raw("s_nop 4")
     lds = LdsCounter()
-    zero = [Ins(f"v_accvgpr_write_b32 {a(DK_BASE + i)}, 0", "accw", [a(DK_BASE + i)])
-            for i in range(128)]
     u1, u2 = units_of((0, 0, 0), None), units_of((0, 1, 1), None)
-    products(st, lds, u1, (0, 0, 0), zero, nxt=(LEAD, u2))
+    products(st, lds, u1, (0, 0, 0), [], nxt=(LEAD, u2))
     wait_lv(st, lds, (0, 0, 0))
     st.raw("s_nop 7", 8)
     st.raw("s_nop 7", 8)

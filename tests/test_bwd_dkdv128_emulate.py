@@ -57,9 +57,12 @@ def expected_bodies(N, k0, causal):
     return out + ["FIN"]
 
 
-def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
+def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale, acc=None):
     """dK, dV [128, 128] (float64, keys past N left 0) of the workgroup whose
-    keys start at k0 (one head)."""
+    keys start at k0 (one head), and the four waves' accumulation registers
+    after the statement.  acc: those registers from a previous run of the
+    statement (another query head of the group), which the kernel passes in
+    unchanged; zero when None."""
     QBASE, OBASE, LBASE, DBASE = 0x10000000, 0x20000000, 0x30000000, 0x40000000
     qb = bf16_bits(q).astype(np.uint16).reshape(-1).view(np.uint8).copy()
     ob = bf16_bits(do).astype(np.uint16).reshape(-1).view(np.uint8).copy()
@@ -97,6 +100,8 @@ def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
     waves = []
     for w in range(4):
         m = Machine()
+        if acc is not None:
+            m.a[G.DK_BASE:G.DV_BASE + 64] = acc[w]
         for lane in range(64):
             h, l32 = lane >> 5, lane & 31
             key = k0 + 32 * w + l32
@@ -166,7 +171,7 @@ def emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale):
                     d = 32 * dbk + 8 * (r // 4) + 4 * h + r % 4
                     dk[32 * w + l32, d] = float(ak[16 * dbk + r]) * scale
                     dv[32 * w + l32, d] = float(av[16 * dbk + r])
-    return dk, dv
+    return dk, dv, [m.a[G.DK_BASE:G.DV_BASE + 64].copy() for m in waves]
 
 
 CASES = [
@@ -194,8 +199,30 @@ def test_generated_dkdv_loop_matches_the_oracle(N, k0, causal):
     lse2 = (rlse[0].astype(np.float32) * np.float32(LOG2E)).astype(np.float32)
     delta = rdelta[0].astype(np.float32)
     PROGRAM.bodies_run.clear()
-    dk, dv = emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale)
+    dk, dv, _ = emulate_dkdv(q, k, v, do, lse2, delta, N, k0, causal, scale)
     assert [b[3:] for b in PROGRAM.bodies_run] == expected_bodies(N, k0, causal), PROGRAM.bodies_run
+    keys = np.arange(k0, min(k0 + BK, N))
+    for got, ref in ((dk, rdk[0]), (dv, rdv[0])):
+        err = np.abs(got[keys - k0] - ref[keys])
+        tol = 2e-2 * max(1.0, float(np.abs(ref[keys]).max()))
+        assert err.max() <= tol and err.mean() <= tol / 10, (err.max(), err.mean(), tol)
+
+
+@pytest.mark.parametrize("N,k0,causal", [(300, 128, True), (330, 0, False)])
+def test_grouped_heads_accumulate_over_statements(N, k0, causal):
+    """Grouped K/V heads: the kernel runs the statement once per query head
+    of the group, passing the accumulators on; the sum over two query heads
+    matches the oracle's grouped-head dK, dV (one K/V parameter used twice)."""
+    q2, _, _ = (t[0].float().numpy() for t in inputs.qkv(1, 2, N, D, torch.bfloat16, seed=N + 11))
+    _, k, v = (t[0, 0].float().numpy() for t in inputs.qkv(1, 1, N, D, torch.bfloat16, seed=N + 12))
+    do2 = inputs.qkv(1, 2, N, D, torch.bfloat16, seed=N + 13)[0][0].float().numpy()
+    scale = D ** -0.5
+    _, rdk, rdv, rlse, rdelta = oracle.backward_gqa(q2, k[None], v[None], do2, scale, causal)
+    acc = None
+    for g in range(2):
+        lse2 = (rlse[g].astype(np.float32) * np.float32(LOG2E)).astype(np.float32)
+        dk, dv, acc = emulate_dkdv(q2[g], k, v, do2[g], lse2, rdelta[g].astype(np.float32), N, k0,
+                                   causal, scale, acc)
     keys = np.arange(k0, min(k0 + BK, N))
     for got, ref in ((dk, rdk[0]), (dv, rdv[0])):
         err = np.abs(got[keys - k0] - ref[keys])

@@ -518,3 +518,35 @@ def test_loop_loads_and_masks(N, causal):
         assert bodies == want + ["FIN"], (N, k0, bodies, want)
         # the straight body is taken for every step it can take
         assert bodies.count("BODY") == max(0, mhi - 3 - mlo)
+
+
+def test_statement_writes_none_of_its_read_only_operands():
+    """With grouped heads the kernel runs the statement once per query head
+    and keeps its plain inputs (addresses, constants) and the K/V rows
+    (in-out operands it must leave unchanged) in place between the runs: no
+    instruction of the statement may write them."""
+    hip = open(os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", "fa_bwd_dkdv128.hip")).read()
+    stmt = hip[hip.index("asm volatile(FA_BWD_DKDV128_LOOP_ASM"):hip.index("FA_BWD_DKDV128_LOOP_CLOBBERS);")]
+    kept = set()
+    for prefix, spec in re.findall(r'"([+=]?)\{([^}]+)\}"\(', stmt):
+        m = re.fullmatch(r"([vas])\[(\d+):(\d+)\]", spec)
+        names = ([f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)]
+                 if m else [spec])
+        kv_rows = prefix == "+" and m is not None and m.group(1) == "a" and int(m.group(2)) >= 128
+        if prefix == "" or kv_rows:
+            kept.update(names)
+    assert {"v160", "a128", "a191", "s64", "s89"} <= kept
+    for l in LINES:
+        if l.endswith(":"):
+            continue
+        op, _, rest = l.partition(" ")
+        if not rest or op.startswith(("s_cmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop",
+                                      "s_barrier", "global_load_lds")):
+            continue
+        if op.startswith("v_cmp") and not op.endswith("_e64"):
+            continue
+        dst = rest.split(",")[0].split(" offset:")[0].strip()
+        m = re.fullmatch(r"([vas])\[(\d+):(\d+)\]", dst)
+        names = [f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)] if m \
+            else [dst]
+        assert not (set(names) & kept), l

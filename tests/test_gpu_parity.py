@@ -371,6 +371,19 @@ def test_backward_resident_dq_grouped_heads(causal, d):
     gqa_parity(2, 130, 26, 333, d, causal, seed=44 + d)
 
 
+@pytest.mark.parametrize("B,H,Hkv,N,causal", [(2, 130, 65, 700, False), (2, 130, 65, 700, True),
+                                              (1, 32, 1, 4096, True)])
+def test_backward_resident_grouped_heads(B, H, Hkv, N, causal):
+    """Grouped K/V heads through the resident dK/dV kernel, which runs its
+    query loop once per query head of an item's group and carries the
+    accumulators: two heads per group, one slice (B2 H130 Hkv65, 780 items);
+    MQA with the group in 16 slices of two heads, partial sums reduced
+    (B1 H32 Hkv1 N4096, 512 items)."""
+    need_gpu()
+    log(f"gqa backward B{B} H{H} Hkv{Hkv} N{N} d128 causal={causal} (resident dK/dV)")
+    gqa_parity(B, H, Hkv, N, 128, causal, seed=N + H + Hkv)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_resident_long(causal):
     """The resident d = 128 backward kernels over long sequences (B2 H16
