@@ -372,7 +372,7 @@ def test_backward_resident_dq_grouped_heads(causal, d):
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,causal", [(2, 130, 65, 700, False), (2, 130, 65, 700, True),
-                                              (1, 32, 1, 4096, True)])
+                                              (1, 32, 1, 4096, True), (1, 32, 1, 4096, False)])
 def test_backward_resident_grouped_heads(B, H, Hkv, N, causal):
     """Grouped K/V heads through the resident dK/dV kernel, which runs its
     query loop once per query head of an item's group and carries the
