@@ -90,7 +90,8 @@ def traffic_bytes(w, which: str) -> float:
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd.hip", "fa_common.hpp"),
     "fwd128_kernel": ("fa_fwd128.hip", "fa_fwd128_loop.inc", "fa_resident.hpp", "fa_common.hpp"),
-    "fwd64_kernel": ("fa_fwd64.hip", "fa_fwd64_loop.inc", "fa_resident.hpp", "fa_common.hpp"),
+    "fwd64_kernel": ("fa_fwd64.hip", "fa_fwd64_loop.inc", "fa_fwd64w2_loop.inc", "fa_resident.hpp",
+                     "fa_common.hpp"),
     "fa_backward": ("fa_bwd.hip", "fa_bwd_dkdv128.hip", "fa_bwd_dkdv128_loop.inc", "fa_bwd_dq128.hip",
                     "fa_bwd_dq128_loop.inc", "fa_resident.hpp", "fa_common.hpp"),
 }

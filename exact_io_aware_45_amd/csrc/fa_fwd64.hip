@@ -7,17 +7,25 @@
 // and "Never write the scores"; "Flash Attention: IO-Aware Attention
 // Computation", paragraph on fused kernels and the online softmax).
 //
-// The structure is the d = 128 kernel's (fa_fwd128.hip): resident 4-wave
-// workgroups, one per CU, taking 256-row query tiles in a serpentine over
-// their XCD's share; 64 query rows per wave for the whole key loop; K two
-// tiles and V one tile ahead by direct loads; the key loop one generated
-// statement (fa_fwd64_loop.inc, from gen_fwd128.py).  At d = 64 a 64-key
-// tile is 16 score and 16 P V products per wave against the same softmax
-// as at d = 128, so the loop is bound by its vector work, which the
-// generator spreads evenly over the products.
+// The structure is the d = 128 kernel's (fa_fwd128.hip): resident
+// workgroups taking query tiles in a serpentine over their XCD's share; 64
+// query rows per wave for the whole key loop; K two tiles and V one tile
+// ahead by direct loads; the key loop one generated statement
+// (fa_fwd64_loop.inc, from gen_fwd128.py).  At d = 64 a 64-key tile is 16
+// score and 16 P V products per wave against the same softmax as at
+// d = 128, so the loop is bound by its vector work, which the generator
+// spreads evenly over the products.
+//
+// Two shapes of workgroup: 4 waves over 256 rows, one workgroup per CU, or
+// 2 waves over 128 rows, two per CU (56 KiB of LDS each; fa_fwd64w2_loop.inc,
+// whose waves issue twice the direct loads).  Both keep one wave per SIMD.
+// The 2-wave one serves causal launches of short sequences: its diagonal
+// band costs two lockstep steps per item instead of four, for a few percent
+// more K/V staging traffic per key.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 #include "fa_fwd64_loop.inc"
+#include "fa_fwd64w2_loop.inc"
 #include "fa_resident.hpp"
 
 #include <algorithm>
@@ -30,27 +38,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int D = 64;
 constexpr int BC = 64;          // keys per tile
-constexpr int NW = 4;           // waves per workgroup
-constexpr int BR = 64 * NW;     // query rows per workgroup
 constexpr int TILE = BC * D;    // elements per K or V tile
 constexpr int TILE_BYTES = TILE * 2;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Direct loads of 64-row tile t (d = 64, bf16) of `src` into the 8 KiB LDS
-// area at byte `lds`: wave w loads rows 16w .. 16w + 15, eight rows per
-// load, chunk q of row r to slot q ^ swz(r); rows past the sequence repeat
-// its last row.
+// area at byte `lds` by an NW-wave workgroup: wave w loads rows
+// (64 / NW) w .. + 64 / NW - 1, eight rows (1 KiB) per load, chunk q of row r
+// to slot q ^ swz(r); rows past the sequence repeat its last row.
+template <int NW>
 __device__ __forceinline__ void dma_tile64(const Shape& sh, int wave, const bf16* src, int t,
                                            uint32_t lds) {
+  constexpr int RW = 64 / NW, NL = RW / 8;
   const int lane = fresh_lane();
   const int rows = min(64, sh.N - t * 64);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 16 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < NL; ++i) {
+    const int row = RW * wave + 8 * i + (lane >> 3);
     const int col = 8 * ((lane & 7) ^ tile_swz<D>(row));
     dma16_untracked(src + (size_t)t * TILE, (uint32_t)(min(row, rows - 1) * D + col) * 2u,
-                    lds + 2048u * wave + 1024u * i);
+                    lds + 1024u * NL * wave + 1024u * i);
   }
 }
 
@@ -66,14 +74,39 @@ __device__ __forceinline__ void dma_rows64(const Shape& sh, const bf16* head, in
   }
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// The generated statement with its operands: the loop of `LOOP`, whose
+// direct-load offsets occupy v[208:GOFF_END] and v[252:GTAIL_END].
+#define FWD64_LOOP_STMT(LOOP, GOFF_END, GTAIL_END) \
+    asm volatile(LOOP##_ASM \
+                 : "={a[0:15]}"(o[0][0]), "={a[16:31]}"(o[0][1]), "={a[32:47]}"(o[1][0]), \
+                   "={a[48:63]}"(o[1][1]), \
+                   "={v212}"(mneg0), "={v213}"(mneg1), "+{v214}"(l0), "+{v215}"(l1), \
+                   "+{v249}"(thr[0]), "+{v250}"(thr[1]), \
+                   "+{s[60:61]}"(kptr), "+{s[62:63]}"(vptr), "+{s71}"(jt) \
+                 : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]), \
+                   "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]), \
+                   "{a[144:147]}"(qf[1][0]), "{a[148:151]}"(qf[1][1]), \
+                   "{a[152:155]}"(qf[1][2]), "{a[156:159]}"(qf[1][3]), \
+                   "{v[192:195]}"(kaddr), "{v[200:203]}"(vaddr), "{v[208:" GOFF_END "]}"(goff), \
+                   "{v224}"(bperm), "{v251}"(ninf), "{v[252:" GTAIL_END "]}"(gtail), \
+                   "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s67}"(slast), "{s68}"(skend), \
+                   "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast), \
+                   "{s83}"(swdiag) \
+                 : LOOP##_CLOBBERS)
+
+template <bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd64_kernel(FwdArgs a) {
+  static_assert(NW == 4 || NW == 2, "4 or 2 waves per workgroup");
+  constexpr int BR = 64 * NW;             // query rows per workgroup
+  constexpr int NL = 8 / NW;              // direct loads per wave and K or V tile
+  typedef __attribute__((ext_vector_type(NL))) uint32_t u32xl;
   // LDS, bytes: [0, 32K) V stage 0, V stage 1, K stage 0, K stage 1 (the
-  // generated loop addresses these directly); [32K, 64K) each wave's 64
-  // query rows; [64K, 80K) each wave's output staging (32 rows).
-  __shared__ __attribute__((aligned(1024))) bf16 smem[10 * TILE];
-  constexpr uint32_t KST0 = 2 * TILE_BYTES, QST0 = 4 * TILE_BYTES, OST0 = 8 * TILE_BYTES;
+  // generated loop addresses these directly); then each wave's 64 query
+  // rows (8 KiB), then each wave's output staging (32 rows, 4 KiB).
+  __shared__ __attribute__((aligned(1024))) bf16 smem[(4 + NW) * TILE + NW * 2048];
+  constexpr uint32_t KST0 = 2 * TILE_BYTES, QST0 = 4 * TILE_BYTES,
+                     OST0 = (4 + NW) * TILE_BYTES;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   auto shape = [&]() { return fresh_shape<BR, BC>(a.N, a.B, a.H, a.Hkv); };
@@ -88,7 +121,7 @@ void fwd64_kernel(FwdArgs a) {
     return CAUSAL ? min(sh.nt, (min(it.q0 + BR, sh.N) - 1) / BC + 1) : sh.nt;
   };
   auto dma_tile = [&](const Shape& sh, const bf16* src, int t, uint32_t stage) {
-    dma_tile64(sh, fresh(wave0), src, t, lds_base() + stage);
+    dma_tile64<NW>(sh, fresh(wave0), src, t, lds_base() + stage);
   };
   auto dma_q = [&](const Shape& sh, const Item& it) {
     const int wave = fresh(wave0);
@@ -163,15 +196,15 @@ void fwd64_kernel(FwdArgs a) {
       vaddr[2 * db] = lds0 + 2u * tr_off(tr_row, sw_lo, db);
       vaddr[2 * db + 1] = lds0 + 2u * tr_off(tr_row + 8, sw_hi, db);
     }
-    // Direct-load offsets within a tile (wave w loads rows 16w .. 16w + 15,
-    // eight rows per load; load i carries instruction offset 1024 i, which
-    // applies to both the global and the LDS address, so it is taken off
-    // here), and for the partial last tile with its rows clamped.
-    u32x2 goff, gtail;
+    // Direct-load offsets within a tile (as dma_tile64: eight rows per load;
+    // load i carries instruction offset 1024 i, which applies to both the
+    // global and the LDS address, so it is taken off here), and for the
+    // partial last tile with its rows clamped.
+    u32xl goff, gtail;
     const int tlast = tend - 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 16 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < NL; ++i) {
+      const int row = 8 * NL * wave + 8 * i + (lane >> 3);
       const int col = 8 * ((lane & 7) ^ tile_swz<D>(row));
       goff[i] = (uint32_t)(row * D + col) * 2u - 1024u * i;
       gtail[i] = (uint32_t)((min(tlast * BC + row, N - 1) - tlast * BC) * D + col) * 2u;
@@ -190,8 +223,8 @@ void fwd64_kernel(FwdArgs a) {
     auto uni64 = [&](uint64_t x) {
       return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x);
     };
-    const uint32_t m0k = uni(lds0 + KST0 + wave * 2048);
-    const uint32_t m0v = uni(lds0 + wave * 2048);
+    const uint32_t m0k = uni(lds0 + KST0 + wave * 1024 * NL);
+    const uint32_t m0v = uni(lds0 + wave * 1024 * NL);
     const uint32_t cbits = uniform_bits(fresh(a.scale) * kLog2e);   // scale * log2(e)
     uint64_t kptr = uni64(reinterpret_cast<uint64_t>(K + 2 * (size_t)TILE));
     uint64_t vptr = uni64(reinterpret_cast<uint64_t>(V + 1 * (size_t)TILE));
@@ -223,22 +256,10 @@ void fwd64_kernel(FwdArgs a) {
     }
     f32x16 o[2][2];
     float mneg0, mneg1, l0 = 0.f, l1 = 0.f;
-    asm volatile(FA_FWD64_LOOP_ASM
-                 : "={a[0:15]}"(o[0][0]), "={a[16:31]}"(o[0][1]), "={a[32:47]}"(o[1][0]),
-                   "={a[48:63]}"(o[1][1]),
-                   "={v212}"(mneg0), "={v213}"(mneg1), "+{v214}"(l0), "+{v215}"(l1),
-                   "+{v249}"(thr[0]), "+{v250}"(thr[1]),
-                   "+{s[60:61]}"(kptr), "+{s[62:63]}"(vptr), "+{s71}"(jt)
-                 : "{a[128:131]}"(qf[0][0]), "{a[132:135]}"(qf[0][1]),
-                   "{a[136:139]}"(qf[0][2]), "{a[140:143]}"(qf[0][3]),
-                   "{a[144:147]}"(qf[1][0]), "{a[148:151]}"(qf[1][1]),
-                   "{a[152:155]}"(qf[1][2]), "{a[156:159]}"(qf[1][3]),
-                   "{v[192:195]}"(kaddr), "{v[200:203]}"(vaddr), "{v[208:209]}"(goff),
-                   "{v224}"(bperm), "{v251}"(ninf), "{v[252:253]}"(gtail),
-                   "{s64}"(m0k), "{s65}"(m0v), "{s66}"(cbits), "{s67}"(slast), "{s68}"(skend),
-                   "{s69}"(sktail), "{s70}"(sfm), "{s72}"(svtail), "{s82}"(sfast),
-                   "{s83}"(swdiag)
-                 : FA_FWD64_LOOP_CLOBBERS);
+    if constexpr (NW == 4)
+      FWD64_LOOP_STMT(FA_FWD64_LOOP, "209", "253");
+    else
+      FWD64_LOOP_STMT(FA_FWD64W2_LOOP, "211", "255");
     const float m_ref[2] = {-mneg0, -mneg1};
     const float lsum[2] = {l0, l1};
 
@@ -305,22 +326,35 @@ void fwd64_kernel(FwdArgs a) {
 }  // namespace
 
 // Whether the hand-scheduled kernel takes this launch: head dim 64, no tile
-// mask, and at least one 256-row workgroup per CU.
+// mask, and at least one 256-row query tile per CU.
 bool fwd64_applies(const FwdArgs& a) {
   if (a.d != 64 || a.mask != nullptr) return false;
-  const long long grid = (long long)((a.N + BR - 1) / BR) * a.B * a.H;
-  return grid >= 256;
+  const long long tiles = (long long)((a.N + 255) / 256) * a.B * a.H;
+  return tiles >= 256;
 }
 
-hipError_t launch_fwd64(const FwdArgs& a, hipStream_t s) {
-  const long long items = (long long)((a.N + BR - 1) / BR) * a.B * a.H;
+namespace {
+
+// Causal sequences up to this length take the 2-wave workgroups: their
+// diagonal band is a large share of the steps (B8 H16 N1024: -7 % kernel
+// time, N4096: -3 %; N16384: +1 %).
+constexpr int kTwoWaveCausalMaxN = 4096;
+
+template <bool CAUSAL, int NW>
+hipError_t launch(const FwdArgs& a, hipStream_t s, int per_cu) {
+  const long long items = (long long)((a.N + 64 * NW - 1) / (64 * NW)) * a.B * a.H;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const long long grid = std::min<long long>(items, resident_cu_count());
-  if (a.causal)
-    hipLaunchKernelGGL((fwd64_kernel<true>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd64_kernel<false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  const long long grid = std::min<long long>(items, (long long)per_cu * resident_cu_count());
+  hipLaunchKernelGGL((fwd64_kernel<CAUSAL, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd64(const FwdArgs& a, hipStream_t s) {
+  if (!a.causal) return launch<false, 4>(a, s, 1);
+  if (a.N <= kTwoWaveCausalMaxN) return launch<true, 2>(a, s, 2);
+  return launch<true, 4>(a, s, 1);
 }
 
 }  // namespace fa

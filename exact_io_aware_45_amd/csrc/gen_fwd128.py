@@ -1,8 +1,9 @@
 """Generate the hand-scheduled main loops of the d = 128 and d = 64 bf16
 forward kernels.
 
-    python exact_io_aware_45_amd/csrc/gen_fwd128.py      # rewrites fa_fwd128_loop.inc
-                                                         # and fa_fwd64_loop.inc
+    python exact_io_aware_45_amd/csrc/gen_fwd128.py      # rewrites fa_fwd128_loop.inc,
+                                                         # fa_fwd64_loop.inc (4 waves)
+                                                         # and fa_fwd64w2_loop.inc (2 waves)
 
 The loop runs inside fa_fwd128.hip (fa_fwd64.hip) as one inline-assembly statement; its
 registers are pinned (the register map below), so the instruction order and
@@ -123,21 +124,26 @@ COST = {"valu": 4.5, "trans": 8.0, "accw": 4.5, "lds": 4.0, "salu": 4.0, "vmem":
 SLOT = 27.0   # vector/LDS issue cycles placed beside one product
 
 
-def configure(d):
-    """Set the module's head-dim dependent values (d = 128 or 64).  At d = 64
-    the vector work of a half-tile (the same as at d = 128) exceeds the
-    shadow of its 16 products, so the slot budget grows to spread it evenly
-    instead of leaving a tail after the last product."""
+def configure(d, nw=4):
+    """Set the module's head-dim dependent values (d = 128 or 64) for a
+    workgroup of `nw` waves (4, or 2 at d = 64).  The waves share each K and
+    V tile's direct loads, so a wave issues 64 d 2 / 1024 / nw of them.  At
+    d = 64 the vector work of a half-tile (the same as at d = 128) exceeds
+    the shadow of its 16 products, so the slot budget grows to spread it
+    evenly instead of leaving a tail after the last product."""
     global D, NC, NDB, NLOAD, OUT, MACRO, KERNEL, STAGE_BYTES, TILE_BYTES, SLOT
-    assert d in (64, 128)
-    D, NC, NDB, NLOAD = d, d // 16, d // 32, d // 32
-    OUT = os.path.join(HERE, f"fa_fwd{d}_loop.inc")
-    MACRO = f"FA_FWD{d}_LOOP"
-    KERNEL = f"fwd{d}_kernel (fa_fwd{d}.hip)"
+    assert (d, nw) in ((128, 4), (64, 4), (64, 2))
+    D, NC, NDB, NLOAD = d, d // 16, d // 32, 64 * d * 2 // 1024 // nw
+    tag = f"{d}" if nw == 4 else f"{d}w{nw}"
+    OUT = os.path.join(HERE, f"fa_fwd{tag}_loop.inc")
+    MACRO = f"FA_FWD{tag.upper()}_LOOP"
+    KERNEL = f"fwd{d}_kernel (fa_fwd{d}.hip" + (")" if nw == 4 else f", {nw} waves)")
     STAGE_BYTES = TILE_BYTES = 64 * d * 2
     SLOT = 27.0 if d == 128 else SLOT64
 
 
+# the (head dim, waves per workgroup) pairs whose loops the kernels include
+VARIANTS = ((128, 4), (64, 4), (64, 2))
 SLOT64 = 40.0
 
 # Hazard distances (in issued instructions; s_nop N counts N+1).
@@ -918,8 +924,8 @@ def render(lines):
 
 def main():
     stale = False
-    for d in (128, 64):
-        configure(d)
+    for d, nw in VARIANTS:
+        configure(d, nw)
         lines = generate()
         text = render(lines)
         if len(sys.argv) > 1 and sys.argv[1] == "--check":

@@ -354,7 +354,7 @@ class Program:
 
 
     def run_workgroup(self, waves, lds, mem):
-        """Run the machines of `waves` (four, one workgroup) to the end, barrier
+        """Run the machines of `waves` (one workgroup) to the end, barrier
         by barrier."""
         pcs = [0] * len(waves)
         while True:

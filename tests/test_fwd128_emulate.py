@@ -2,8 +2,8 @@
 forward kernels.
 
 The instruction text that gen_fwd128.py emits (fa_fwd128_loop.inc,
-fa_fwd64_loop.inc) is executed for the four waves of one workgroup by the
-emulator in _emu.py (registers, LDS, bounds-checked K/V buffers, barriers).
+fa_fwd64_loop.inc, and fa_fwd64w2_loop.inc for 2-wave workgroups) is
+executed for the waves of one workgroup by the emulator in _emu.py (registers, LDS, bounds-checked K/V buffers, barriers).
 The setup (registers and the three tiles staged before the loop) restates
 the C++ of fa_fwd128.hip / fa_fwd64.hip.  The output is normalised as the kernel's epilogue does and
 compared with the fp64 oracle at the bf16 tolerances.  Hazards and timing
@@ -22,21 +22,23 @@ from _emu import Machine, Memory, Program, bf16_bits, bf16_to_f32
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEN = os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", "gen_fwd128.py")
-BC, BR = 64, 256
+BC = 64
+# generated loops: head dim and waves per workgroup ("64w2": d = 64, 2 waves)
+VARIANTS = {128: (128, 4), 64: (64, 4), "64w2": (64, 2)}
 
 
-def load_gen(d):
-    spec = importlib.util.spec_from_file_location(f"gen_fwd_emu{d}", GEN)
+def load_gen(d, nw):
+    spec = importlib.util.spec_from_file_location(f"gen_fwd_emu{d}w{nw}", GEN)
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    mod.configure(d)
+    mod.configure(d, nw)
     return mod
 
 
-GENS = {d: load_gen(d) for d in (128, 64)}
-PROGRAMS = {d: Program(G.generate(), ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN", "FA_IDLEA",
-                                      "FA_IDLEB"), "FA_SLOW")
-            for d, G in GENS.items()}
+GENS = {key: load_gen(*dn) for key, dn in VARIANTS.items()}
+PROGRAMS = {key: Program(G.generate(), ("FA_BODY", "FA_GB", "FA_ITM", "FA_FIN", "FA_IDLEA",
+                                        "FA_IDLEB"), "FA_SLOW")
+            for key, G in GENS.items()}
 
 
 def swz_of(D):
@@ -46,12 +48,15 @@ def swz_of(D):
     return lambda r: 4 * ((r >> 1) & 1) + ((r >> 2) & 3)
 
 
-def emulate_workgroup(q, k, v, N, q0, causal, scale, D=128):
-    """Run the generated loop for the workgroup whose rows start at q0 (one
-    head); returns O [256, D] (float64, rows past N left 0) and LSE."""
-    G, PROGRAM, tile_swz = GENS[D], PROGRAMS[D], swz_of(D)
-    NC, NDB, NLOAD = D // 16, D // 32, D // 32
+def emulate_workgroup(q, k, v, N, q0, causal, scale, key=128):
+    """Run the generated loop `key` for the workgroup whose rows start at q0
+    (one head); returns O [64 NW, D] (float64, rows past N left 0) and LSE."""
+    D, NW = VARIANTS[key]
+    G, PROGRAM, tile_swz = GENS[key], PROGRAMS[key], swz_of(D)
+    BR = 64 * NW
+    NC, NDB, NLOAD = D // 16, D // 32, 64 * D * 2 // 1024 // NW
     LPR = D // 8             # lanes (16-byte chunks) per tile row in a direct load
+    RW = 64 // NW            # tile rows each wave loads
     KBASE, VBASE = 0x10000000, 0x20000000
     kb = bf16_bits(k).astype(np.uint16).reshape(-1).view(np.uint8).copy()
     vb = bf16_bits(v).astype(np.uint16).reshape(-1).view(np.uint8).copy()
@@ -84,7 +89,7 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale, D=128):
     if tend > 1:
         load_tile(kb, 1, 3 * TILE * 2)
     waves = []
-    for w in range(4):
+    for w in range(NW):
         m = Machine()
         wrow0 = q0 + 64 * w
         for lane in range(64):
@@ -109,7 +114,7 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale, D=128):
                 m.v[G.VADDR + 2 * db, lane] = 2 * tr_off(tr_row, sw_lo, db)
                 m.v[G.VADDR + 2 * db + 1, lane] = 2 * tr_off(tr_row + 8, sw_hi, db)
             for i in range(NLOAD):
-                row = 16 * w + (BC // 4 // NLOAD) * i + lane // LPR
+                row = RW * w + (RW // NLOAD) * i + lane // LPR
                 col = 8 * ((lane % LPR) ^ tile_swz(row))
                 m.v[G.GOFF + i, lane] = (row * D + col) * 2 - 1024 * i
                 m.v[G.GOFF_TAIL + i, lane] = ((min(tlast * BC + row, N - 1) - tlast * BC) * D
@@ -123,8 +128,8 @@ def emulate_workgroup(q, k, v, N, q0, causal, scale, D=128):
         kp, vp = KBASE + 2 * TILE * 2, VBASE + TILE * 2
         m.s[G.S_KPTR], m.s[G.S_KPTR + 1] = kp & 0xFFFFFFFF, kp >> 32
         m.s[G.S_VPTR], m.s[G.S_VPTR + 1] = vp & 0xFFFFFFFF, vp >> 32
-        m.s[G.S_M0K] = 2 * TILE * 2 + w * 32 * D
-        m.s[G.S_M0V] = w * 32 * D
+        m.s[G.S_M0K] = 2 * TILE * 2 + w * RW * D * 2
+        m.s[G.S_M0V] = w * RW * D * 2
         m.s[G.S_C] = int(np.float32(sl2).view(np.uint32))
         tail = ragged and tend == nt
         m.s[G.S_LAST] = tend - 1
@@ -177,7 +182,7 @@ def wave_last_tile(N, q0, w, tend, causal):
     return min(tend - 1, min(q0 + 64 * w + 63, N - 1) // BC) if causal else tend - 1
 
 
-def expected_bodies(N, q0, causal, w=0):
+def expected_bodies(N, q0, causal, w=0, BR=256):
     """Which body each tile step of wave w should take: straight while the
     next tile is unmasked and both loads are whole tiles, the masked body
     when the next tile needs a mask, the general one otherwise, the final
@@ -207,12 +212,14 @@ def expected_bodies(N, q0, causal, w=0):
     return out + ["IDLE" if tend - 1 > last else "FIN"]
 
 
-@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("key", list(VARIANTS))
 @pytest.mark.parametrize("N,q0,causal,kscale", CASES)
-def test_generated_loop_matches_the_oracle(N, q0, causal, kscale, D):
+def test_generated_loop_matches_the_oracle(N, q0, causal, kscale, key):
+    D, NW = VARIANTS[key]
+    BR = 64 * NW
     q, k, v = (t[0, 0].float().numpy() for t in inputs.qkv(1, 1, N, D, torch.bfloat16,
                                                              seed=N + q0 + int(causal)))
-    PROGRAM = PROGRAMS[D]
+    PROGRAM = PROGRAMS[key]
     if kscale != 1.0:
         k[192:] *= kscale
         k = bf16_to_f32(bf16_bits(k))
@@ -220,10 +227,10 @@ def test_generated_loop_matches_the_oracle(N, q0, causal, kscale, D):
     PROGRAM.slow_taken = 0
     PROGRAM.bodies_run.clear()
     PROGRAM.bodies_by_wave.clear()
-    O, L = emulate_workgroup(q, k, v, N, q0, causal, scale, D)
-    for w in range(4):
+    O, L = emulate_workgroup(q, k, v, N, q0, causal, scale, key)
+    for w in range(NW):
         got = [b[3:7] if b.startswith("FA_IDLE") else b[3:] for b in PROGRAM.bodies_by_wave[w]]
-        assert got == expected_bodies(N, q0, causal, w), (w, got)
+        assert got == expected_bodies(N, q0, causal, w, BR), (w, got)
     # keys scaled by 3 from key 192 on lift those tiles' weights far past 2^8
     # above the reference set by tile 0: the exact slow path must run there
     assert (PROGRAM.slow_taken > 0) == (kscale != 1.0), PROGRAM.slow_taken

@@ -1,6 +1,6 @@
 """Host-side model of the generated main loops of the d = 128 and d = 64
 forward kernels (exact_io_aware_45_amd/csrc/gen_fwd128.py -> fa_fwd128_loop.inc,
-fa_fwd64_loop.inc), CPU only.
+fa_fwd64_loop.inc, fa_fwd64w2_loop.inc), CPU only.
 
 The emitted instruction text is parsed and executed on a model of one
 workgroup's LDS and registers:
@@ -30,14 +30,16 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEN = os.path.join(ROOT, "exact_io_aware_45_amd", "csrc", "gen_fwd128.py")
-DIMS = [128, 64]
+# generated loops: head dim and waves per workgroup ("64w2": d = 64, 2 waves)
+VARIANTS = {128: (128, 4), 64: (64, 4), "64w2": (64, 2)}
+DIMS = list(VARIANTS)
 
 
-def load_gen(d):
-    spec = importlib.util.spec_from_file_location(f"gen_fwd_sched{d}", GEN)
+def load_gen(d, nw):
+    spec = importlib.util.spec_from_file_location(f"gen_fwd_sched{d}w{nw}", GEN)
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    mod.configure(d)
+    mod.configure(d, nw)
     return mod
 
 
@@ -49,17 +51,21 @@ def swz_of(D):
 
 
 class Loop:
-    """One head dim's generated statement and the kernel's per-lane values."""
+    """One generated statement (head dim, waves per workgroup) and the
+    kernel's per-lane values."""
 
-    def __init__(self, d):
-        self.D = d
-        self.G = load_gen(d)
+    def __init__(self, key):
+        d, nw = VARIANTS[key]
+        self.D, self.NW, self.BR = d, nw, 64 * nw
+        self.G = load_gen(d, nw)
         self.LINES = self.G.generate()
-        self.NC, self.NDB, self.NLOAD = d // 16, d // 32, d // 32
+        self.NC, self.NDB = d // 16, d // 32
+        self.NLOAD = 64 * d * 2 // 1024 // nw   # 1 KiB direct loads per wave and tile
         self.LPR = d // 8                 # 16-byte chunks per tile row
         self.RPL = 64 // self.LPR         # tile rows per direct load
+        self.RW = 64 // nw                # tile rows each wave loads
         self.STAGE = 64 * d * 2           # bytes of one K or V stage
-        self.WAVE = 32 * d                # bytes of one wave's 16 rows of a tile
+        self.WAVE = self.RW * d * 2       # bytes of one wave's rows of a tile
         self.M0K = 2 * self.STAGE         # LDS byte address of K stage 0 (+ wave * WAVE in s64)
         self.M0V = 0
         self.swz = swz_of(d)
@@ -89,11 +95,11 @@ class Loop:
             for db in range(self.NDB):
                 vaddr[2 * db, lane] = 2 * tr_off(tr_row, sw_lo, db)
                 vaddr[2 * db + 1, lane] = 2 * tr_off(tr_row + 8, sw_hi, db)
-        goff = np.zeros((4, self.NLOAD, 64), np.int64)   # [wave][load][lane]
-        for w in range(4):
+        goff = np.zeros((self.NW, self.NLOAD, 64), np.int64)   # [wave][load][lane]
+        for w in range(self.NW):
             for i in range(self.NLOAD):
                 for lane in range(64):
-                    row = 16 * w + self.RPL * i + lane // self.LPR
+                    row = self.RW * w + self.RPL * i + lane // self.LPR
                     col = 8 * ((lane % self.LPR) ^ tile_swz(row))
                     goff[w, i, lane] = 2 * (row * D + col) - 1024 * i
         return kaddr, vaddr, goff
@@ -109,7 +115,7 @@ class Loop:
         return out
 
 
-LOOPS = {d: Loop(d) for d in DIMS}
+LOOPS = {key: Loop(key) for key in DIMS}
 
 
 @pytest.mark.parametrize("d", DIMS)
@@ -198,14 +204,14 @@ def env_of(L, case):
 
 
 def stage_tiles(L, lines, ktile, vtile, tail_offs=None):
-    """Execute the direct loads in `lines` for all four waves into a 64 KiB LDS
+    """Execute the direct loads in `lines` for all waves into a 64 KiB LDS
     image (uint16 elements): whole-tile loads use the kernel's offsets, the
     clamped ones `tail_offs`; the instruction offset applies to both
     addresses.  Returns the image and {(K|V, stage, clamped)} loaded."""
     G = L.G
     lds = np.full(32768, -1, np.int64)
     loaded = set()
-    for w in range(4):
+    for w in range(L.NW):
         m0 = None
         for l in lines:
             op, args = split(l)
@@ -372,11 +378,11 @@ def test_operands_of_the_first_tile_scores(d):
 def tail_offsets(L, N, tlast):
     """Clamped direct-load offsets of the partial last tile (the kernel's
     formula): rows past N - 1 repeat row N - 1."""
-    out = np.zeros((4, L.NLOAD, 64), np.int64)
-    for w in range(4):
+    out = np.zeros((L.NW, L.NLOAD, 64), np.int64)
+    for w in range(L.NW):
         for i in range(L.NLOAD):
             for lane in range(64):
-                row = 16 * w + L.RPL * i + lane // L.LPR
+                row = L.RW * w + L.RPL * i + lane // L.LPR
                 col = 8 * ((lane % L.LPR) ^ L.swz(row))
                 out[w, i, lane] = 2 * ((min(tlast * 64 + row, N - 1) - tlast * 64) * L.D + col)
     return out
@@ -388,7 +394,7 @@ def tail_offsets(L, N, tlast):
 def test_direct_loads_place_tiles_as_the_reads_expect(name, case, d):
     """The emitted loads (M0 values, offset registers, instruction offsets)
     write chunk q of tile row r to slot q ^ swz(r) of the right stage, for
-    all four waves, and cover each loaded stage exactly once; a partial last
+    all waves, and cover each loaded stage exactly once; a partial last
     tile (here 37 rows) goes through the clamped offsets, its missing rows
     repeating the last one; a tile past the end is not loaded."""
     L = LOOPS[d]
@@ -670,7 +676,7 @@ def run_control(L, N, q0, causal, w=0):
     (and whether through the clamped offsets), which tiles get masked, which
     body each step takes, how many barriers the wave meets."""
     G, LINES = L.G, L.LINES
-    BC, BR = 64, 256
+    BC, BR = 64, L.BR
     nt = -(-N // BC)
     qmax = min(q0 + BR, N) - 1
     tend = min(nt, qmax // BC + 1) if causal else nt
@@ -747,10 +753,10 @@ def test_loop_loads_and_masks(N, causal, d):
     to the one after the wave's last visible tile; every step before the
     last takes the straight body when its next tile is unmasked and both its
     loads are whole tiles, and steps past the wave's last visible tile are
-    idle (never a straight one); all four waves meet the same barriers."""
-    for q0 in range(0, N, 256):
+    idle (never a straight one); all waves meet the same barriers."""
+    for q0 in range(0, N, LOOPS[d].BR):
         nbar = set()
-        for w in range(4):
+        for w in range(LOOPS[d].NW):
             tend, fm, kload, vload, masked, bodies, barriers = run_control(LOOPS[d], N, q0,
                                                                            causal, w)
             nbar.add(barriers)
