@@ -195,6 +195,18 @@ def test_forward_resident_grid(N, causal, d):
     forward_parity_all_heads(q, k, v, causal, chunk=130)
 
 
+@pytest.mark.parametrize("N", [4096, 4097])
+def test_forward_d64_causal_workgroup_shapes(N):
+    """Causal d = 64 at the longest sequence that takes the 2-wave, 128-row
+    workgroups (N = 4096) and one past it (4-wave, 256-row workgroups, with a
+    ragged last tile): B1 H16 gives at least 256 query tiles of 256 rows, so
+    both take the resident kernel; every head against the oracle."""
+    need_gpu()
+    log(f"forward bf16 B1 H16 N{N} d64 causal (2-wave / 4-wave boundary)")
+    q, k, v = inputs.qkv(1, 16, N, 64, torch.bfloat16, seed=3000 + N)
+    forward_parity_all_heads(q, k, v, True, chunk=4)
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [700, 1500])
