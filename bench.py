@@ -448,8 +448,10 @@ def main():
                       "(1 launch per fa_forward_fp8)")
     elif uses_resident_fwd(w):
         entry = "_gqa" if w.Hkv else ""
-        fwd_kernel = (f"fwd{w.d}_kernel<{mode}> (1 launch per fa_forward{entry}; one resident "
-                      "4-wave workgroup per CU, 256-row query tiles)")
+        shape = ("two resident 2-wave workgroups per CU, 128-row query tiles"
+                 if w.d == 64 and w.causal and w.N <= 4096 else
+                 "one resident 4-wave workgroup per CU, 256-row query tiles")
+        fwd_kernel = f"fwd{w.d}_kernel<{mode}> (1 launch per fa_forward{entry}; {shape})"
     else:
         entry = "_blocksparse" if w.sparse else ("_gqa" if w.Hkv else "")
         fwd_kernel = (f"fwd_bf16_kernel<d={w.d}, BC=64, {nw} waves, {mode}> "
