@@ -203,8 +203,10 @@ def sustained_clock(step, seconds: float):
                                 "of untimed steps run after the timed ones")
 
 
-def cpu_baseline(w, inp, passes, mask=None, budget_s: float = 15.0, max_heads: int = 32):
-    """Time the fp64 oracle (the same passes, whole heads) on the host cores."""
+def cpu_baseline(w, inp, passes, mask=None, budget_s: float = 25.0, max_heads: int = 32):
+    """Time the fp64 oracle (the same passes, whole heads) on the host cores:
+    heads in turn until `max_heads` or `budget_s` seconds (all 32 heads of the
+    long workload take about 17 s on 16 threads)."""
     import oracle
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
     oracle.build(force=False)
