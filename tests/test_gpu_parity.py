@@ -195,6 +195,32 @@ def test_forward_resident_grid(N, causal, d):
     forward_parity_all_heads(q, k, v, causal, chunk=130)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_resident_grid_odd_item_count(causal, d):
+    """B1 H261 N300: 522 query tiles of 256 rows (783 of 128 rows), a count
+    that is no multiple of the 8 XCDs, so the resident kernels hand out their
+    items by the plain serpentine over all workgroups instead of per-XCD
+    shares; every head against the oracle."""
+    need_gpu()
+    log(f"forward bf16 B1 H261 N300 d{d} causal={causal} (item count not a multiple of 8)")
+    q, k, v = inputs.qkv(1, 261, 300, d, torch.bfloat16, seed=4000 + d + int(causal))
+    forward_parity_all_heads(q, k, v, causal, chunk=87)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_resident_odd_item_count(causal):
+    """B1 H261 N300 d128: 783 dK/dV items of 128 keys and 522 dQ items of 256
+    rows, neither a multiple of the 8 XCDs, so both resident backward kernels
+    use the plain serpentine over all workgroups; every gradient of every
+    head against the oracle."""
+    need_gpu()
+    log(f"backward bf16 B1 H261 N300 d128 causal={causal} (item counts not multiples of 8)")
+    q, k, v, do = inputs.qkv(1, 261, 300, 128, torch.bfloat16, seed=4100 + int(causal),
+                             with_dout=True)
+    backward_parity_all_heads(q, k, v, do, causal, chunk=87)
+
+
 @pytest.mark.parametrize("N", [4096, 4097])
 def test_forward_d64_causal_workgroup_shapes(N):
     """Causal d = 64 at the longest sequence that takes the 2-wave, 128-row
