@@ -208,6 +208,18 @@ def test_forward_resident_grid_odd_item_count(causal, d):
     forward_parity_all_heads(q, k, v, causal, chunk=87)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("H", [255, 256])
+def test_forward_resident_threshold(H, d):
+    """B1 N256: H 255 gives 255 query tiles of 256 rows (the compiler-scheduled
+    kernel), H 256 gives 256 (the first grid the resident kernel takes); both
+    sides of the switch against the oracle, causal."""
+    need_gpu()
+    log(f"forward bf16 B1 H{H} N256 d{d} causal (resident threshold)")
+    q, k, v = inputs.qkv(1, H, 256, d, torch.bfloat16, seed=4200 + H + d)
+    forward_parity_all_heads(q, k, v, True, chunk=64)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_resident_odd_item_count(causal):
     """B1 H261 N300 d128: 783 dK/dV items of 128 keys and 522 dQ items of 256
