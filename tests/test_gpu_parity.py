@@ -220,6 +220,18 @@ def test_forward_resident_threshold(H, d):
     forward_parity_all_heads(q, k, v, True, chunk=64)
 
 
+@pytest.mark.parametrize("H", [127, 128, 256])
+def test_backward_resident_threshold(H):
+    """B1 N256 d128 causal: H 127 gives 254 dK/dV items of 128 keys (both
+    passes compiler-scheduled), H 128 gives 256 (the resident dK/dV kernel,
+    with 128 dQ items still compiler-scheduled), H 256 makes both resident;
+    every gradient against the oracle."""
+    need_gpu()
+    log(f"backward bf16 B1 H{H} N256 d128 causal (resident thresholds)")
+    q, k, v, do = inputs.qkv(1, H, 256, 128, torch.bfloat16, seed=4300 + H, with_dout=True)
+    backward_parity_all_heads(q, k, v, do, True, chunk=64)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_resident_odd_item_count(causal):
     """B1 H261 N300 d128: 783 dK/dV items of 128 keys and 522 dQ items of 256
